@@ -1,0 +1,25 @@
+"""Plain, slow, obviously-correct fp64 CPU attention oracle.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import anything from this package.  The
+GPU path (``exact_tiled_attention_14_amd``) never imports it and it imports
+nothing from the GPU path: the two share no kernels, helpers, tables or
+pre/post-processing.  Inputs come from ``workloads`` (seeded generators that do
+no attention arithmetic) or from the tests themselves.
+
+Every function here is pinned by a ``-m "not gpu"`` test in ``tests/`` against
+something other than itself (closed forms, invariants, a library routine,
+brute force over every block size); see ``tests/test_oracle_pins.py`` and
+``tests/test_oracle_blockwise.py``.  No function here is "parity unpinned".
+"""
+
+from .attention import (  # noqa: F401
+    admissible,
+    attention,
+    blockwise_attention,
+    kv_head_of,
+    merge_partials,
+    merge_softmax,
+    scores,
+    softmax_rows,
+)

@@ -1,0 +1,214 @@
+"""fp64 attention written out from its definition, plus the tiled recurrence.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): nothing on the GPU path
+may import this module.
+
+Sources (web pages on exact tiled attention):
+
+* "AI训练的最大障碍不是算力,而是“内存墙”" (zsdodo.com): the code block of
+  standard PyTorch attention (scores = Q·Kᵀ/√d_k, softmax over the key axis,
+  weights·V) and the ``safe_softmax_block`` code block (running max m and
+  running exponent sum ℓ).
+* "闪电注意力：革命性地提高Transformer效率" (unite.ai): section "闪电注意力的数学原理"
+  (softmax decomposition, formula 1, and softmax merge, formula 2) and section
+  "闪电注意力算法" (outer loop over K/V blocks, inner loop over Q blocks).
+* "第四章 注意力机制实战案例" (aiknowledge.cn), §4.1.3: accumulated output scaled by
+  α = exp(m_old − m_new) plus exp(S − m_new)·V, tail blocks cut with min(), and
+  one division by the running sum at the end.
+* aifi multi-head attention page (qqiyuan.cn), section "动态序列处理": padded
+  positions are ignored through an attention mask.
+* same unite.ai page, section "闪电注意力-2": grouped-query attention.
+
+Readings where the pages are silent (each listed in the design doc):
+causal admits keys j ≤ i; key padding admits j < key_len_b; grouped query
+heads map to kv head h // (H / Hkv); a row with no admissible key has O = 0
+and LSE = −∞; LSE is the natural-log log-sum-exp m + ln ℓ of the scaled
+scores; ``scale`` is used exactly as passed (callers pass the fp32 value the
+GPU receives).
+"""
+
+import numpy as np
+
+__all__ = [
+    "kv_head_of",
+    "admissible",
+    "scores",
+    "softmax_rows",
+    "attention",
+    "blockwise_attention",
+    "merge_partials",
+    "merge_softmax",
+]
+
+
+def _f64(x):
+    """Exact upcast of a float array (fp32 or bf16-valued fp32) to fp64."""
+    return np.asarray(x, dtype=np.float64)
+
+
+def kv_head_of(h, H, Hkv):
+    """KV head read by query head ``h``: consecutive groups of H/Hkv query
+    heads share one KV head (grouped-query attention, unite.ai page, section
+    "闪电注意力-2"; the grouping rule itself is a reading)."""
+    return h // (H // Hkv)
+
+
+def admissible(rows, n_keys, causal):
+    """Boolean [len(rows), n_keys]: key j is admissible for query row i.
+
+    ``n_keys`` is already cut to the sequence's key length, so padding is
+    handled by the caller truncating K and V (padded positions are ignored,
+    aifi page, section "动态序列处理").  Causal keeps j ≤ i (a reading: no page
+    defines a causal mask)."""
+    rows = np.asarray(rows)
+    ok = np.ones((rows.shape[0], n_keys), dtype=bool)
+    if causal:
+        ok &= np.arange(n_keys)[None, :] <= rows[:, None]
+    return ok
+
+
+def scores(q_rows, k_valid, scale):
+    """S = scale · Q Kᵀ for the given query rows against the valid keys
+    (step 1 of standard attention, zsdodo page)."""
+    return scale * (_f64(q_rows) @ _f64(k_valid).T)
+
+
+def softmax_rows(s):
+    """Row softmax with the row max subtracted first (unite.ai page, section
+    "闪电注意力的数学原理", formula 1: softmax(x) = exp(x − m)/Σ exp(x − m)).
+
+    ``s`` is fp64 [R, n] with −∞ at inadmissible keys.  Returns
+    (P, m, ℓ): P the normalised weights, m the row max, ℓ = Σ exp(s − m).
+    A row with no finite entry gets P = 0, m = −∞, ℓ = 0."""
+    s = _f64(s)
+    if s.shape[1] == 0:
+        r = s.shape[0]
+        return np.zeros_like(s), np.full(r, -np.inf), np.zeros(r)
+    m = s.max(axis=1)
+    empty = m == -np.inf
+    e = np.exp(s - np.where(empty, 0.0, m)[:, None])
+    ell = e.sum(axis=1)
+    p = e / np.where(empty, 1.0, ell)[:, None]
+    return p, m, ell
+
+
+def attention(q, k, v, scale, causal=False, key_lens=None, rows=None, row_chunk=512):
+    """Exact attention, materialising S one chunk of query rows at a time.
+
+    q: [B, H, N, d]; k, v: [B, Hkv, N, d] (any float dtype, upcast exactly to
+    fp64).  key_lens: None or length-B integers (clamped to [0, N]).
+    rows: None (all N query rows) or a 1-D array of query-row indices, the
+    same for every (b, h) — row sampling is exact because softmax is taken
+    row by row (the aifi and Blockwise Parallel Transformer pages both chunk
+    the queries while keeping all keys).
+
+    Returns (O, LSE): O fp64 [B, H, R, d], LSE fp64 [B, H, R] with
+    LSE_i = m_i + ln ℓ_i (natural log), R = number of rows.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    assert k.shape == (B, Hkv, N, d) and v.shape == k.shape and H % Hkv == 0
+    rows = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
+    R = rows.shape[0]
+    O = np.zeros((B, H, R, d))
+    LSE = np.full((B, H, R), -np.inf)
+    for b in range(B):
+        kl = N if key_lens is None else int(min(max(int(key_lens[b]), 0), N))
+        for h in range(H):
+            g = kv_head_of(h, H, Hkv)
+            k_valid = k[b, g, :kl]
+            v_valid = v[b, g, :kl]
+            for c0 in range(0, R, row_chunk):
+                r = rows[c0:c0 + row_chunk]
+                s = scores(q[b, h, r], k_valid, scale)
+                s = np.where(admissible(r, kl, causal), s, -np.inf)
+                p, m, ell = softmax_rows(s)
+                O[b, h, c0:c0 + len(r)] = p @ v_valid
+                live = m > -np.inf
+                LSE[b, h, c0:c0 + len(r)] = np.where(
+                    live, m + np.log(np.where(live, ell, 1.0)), -np.inf)
+    return O, LSE
+
+
+def blockwise_attention(q, k, v, scale, block_q, block_k, causal=False,
+                        key_lens=None, kv_outer=False):
+    """The tiled forward pass, one (query block, key block) pair at a time.
+
+    For each pair: S_blk = scale·Q_blk K_blkᵀ (inadmissible → −∞);
+    m_new = max(m, rowmax S_blk); P = exp(S_blk − m_new);
+    ℓ_new = exp(m − m_new)·ℓ + rowsum P (``safe_softmax_block``, zsdodo page);
+    O ← exp(m − m_new)·O + P·V_blk (aiknowledge.cn §4.1.3); after the last
+    block O ← O/ℓ and LSE = m + ln ℓ.  Tail blocks are cut at the sequence
+    end.  ``kv_outer`` swaps the loops to the key-block-outer order of the
+    unite.ai page, section "闪电注意力算法".  A row that has seen no admissible
+    key keeps m = −∞; its exponent offset is taken as 0 so that no
+    exp(−∞ − (−∞)) arises (a reading: the pages are silent).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    O_out = np.zeros((B, H, N, d))
+    LSE_out = np.full((B, H, N), -np.inf)
+    for b in range(B):
+        kl = N if key_lens is None else int(min(max(int(key_lens[b]), 0), N))
+        for h in range(H):
+            g = kv_head_of(h, H, Hkv)
+            m = np.full(N, -np.inf)
+            ell = np.zeros(N)
+            acc = np.zeros((N, d))
+            qb = [(i0, min(i0 + block_q, N)) for i0 in range(0, N, block_q)]
+            kb = [(j0, min(j0 + block_k, kl)) for j0 in range(0, kl, block_k)]
+            pairs = ([(i, j) for j in kb for i in qb] if kv_outer
+                     else [(i, j) for i in qb for j in kb])
+            for (i0, i1), (j0, j1) in pairs:
+                s = scale * (q[b, h, i0:i1] @ k[b, g, j0:j1].T)
+                if causal:
+                    ii = np.arange(i0, i1)[:, None]
+                    jj = np.arange(j0, j1)[None, :]
+                    s = np.where(jj <= ii, s, -np.inf)
+                m_old = m[i0:i1]
+                m_new = np.maximum(m_old, s.max(axis=1))
+                off = np.where(m_new == -np.inf, 0.0, m_new)
+                p = np.exp(s - off[:, None])
+                alpha = np.exp(m_old - off)
+                ell[i0:i1] = alpha * ell[i0:i1] + p.sum(axis=1)
+                acc[i0:i1] = alpha[:, None] * acc[i0:i1] + p @ v[b, g, j0:j1]
+                m[i0:i1] = m_new
+            live = ell > 0
+            O_out[b, h] = acc / np.where(live, ell, 1.0)[:, None]
+            LSE_out[b, h] = np.where(live, m + np.log(np.where(live, ell, 1.0)), -np.inf)
+    return O_out, LSE_out
+
+
+def merge_partials(o_x, lse_x, o_y, lse_y):
+    """Combine two attention results taken over disjoint key sets X and Y.
+
+    Reading of the garbled softmax-merge formula (unite.ai page, section
+    "闪电注意力的数学原理", formula 2): with LSE = ln(e^{LSE_x} + e^{LSE_y}),
+    O = e^{LSE_x − LSE}·O_x + e^{LSE_y − LSE}·O_y.  Either side may be empty
+    (LSE = −∞, O = 0)."""
+    o_x, o_y = _f64(o_x), _f64(o_y)
+    lse_x, lse_y = _f64(lse_x), _f64(lse_y)
+    lse = np.logaddexp(lse_x, lse_y)
+    live = lse > -np.inf
+    ref = np.where(live, lse, 0.0)
+    wx = np.where(live, np.exp(lse_x - ref), 0.0)
+    wy = np.where(live, np.exp(lse_y - ref), 0.0)
+    return wx[..., None] * o_x + wy[..., None] * o_y, lse
+
+
+def merge_softmax(x, y):
+    """softmax of the concatenation [x, y] from the two halves' statistics.
+
+    With m = max(m_x, m_y) and ℓ = e^{m_x−m}ℓ_x + e^{m_y−m}ℓ_y, the result is
+    [e^{m_x−m}ℓ_x·softmax(x), e^{m_y−m}ℓ_y·softmax(y)] / ℓ (the corrected
+    reading of formula 2 in section "闪电注意力的数学原理" of the unite.ai page).
+    x, y: 1-D score vectors, each with at least one finite entry."""
+    px, mx, lx = softmax_rows(_f64(x)[None, :])
+    py, my, ly = softmax_rows(_f64(y)[None, :])
+    m = np.maximum(mx, my)
+    wx = np.exp(mx - m) * lx
+    wy = np.exp(my - m) * ly
+    ell = wx + wy
+    return np.concatenate([wx[:, None] * px, wy[:, None] * py], axis=1)[0] / ell[0]

@@ -1,0 +1,80 @@
+"""Seeded synthetic inputs for the attention forward pass.
+
+This module is shared by the tests, ``bench.py`` and ``smoke()``: it feeds the
+same tensors to the GPU path and to the fp64 oracle.  It holds shapes and random
+draws only — no attention arithmetic — and imports neither the oracle nor the
+GPU package.
+
+Recipe (stated once, used everywhere): a ``torch.Generator('cpu')`` seeded with
+the workload's seed draws Q, K and V, in that order, as i.i.d. N(0, 1) float32
+with ``torch.randn``; bf16 workloads then round them to bfloat16 (round to
+nearest even).  A padded workload draws its per-sequence key lengths last from
+the same generator, uniform on the integers N/2 .. N inclusive.  The softmax
+scale is 1/sqrt(head_dim) rounded to float32, the value the GPU receives.
+"""
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    Hkv: int
+    N: int
+    d: int
+    dtype: str          # "f32" or "bf16": storage type of q, k, v, o
+    causal: bool
+    padded: bool        # per-sequence key lengths with a key padding mask
+    seed: int
+
+    @property
+    def scale(self):
+        return float(np.float32(1.0 / math.sqrt(self.d)))
+
+
+# The five workloads the attention pages' examples are sized like: a small
+# fp32 single-head case, multi-head at N=1024, d_model=512 split 8x64 at
+# N=4096 (the memory-wall analysis size), a long causal sequence, and a
+# grouped-query padded batch.
+WORKLOADS = {
+    1: Workload("fp32 single-head B1 H1 N256 d64", 1, 1, 1, 256, 64, "f32", False, False, 1),
+    2: Workload("mha B4 H8 N1024 d64 bf16", 4, 8, 8, 1024, 64, "bf16", False, False, 2),
+    3: Workload("causal B2 H8 N4096 d64 bf16", 2, 8, 8, 4096, 64, "bf16", True, False, 3),
+    4: Workload("causal long B1 H16 N16384 d128 bf16", 1, 16, 16, 16384, 128, "bf16", True, False, 4),
+    5: Workload("gqa padded B2 Hq32 Hkv8 N8192 d128 bf16", 2, 32, 8, 8192, 128, "bf16", False, True, 5),
+}
+
+
+def make_qkv(B, H, Hkv, N, d, dtype="bf16", seed=0, padded=False):
+    """Draw (q, k, v, key_lens) on the CPU following the recipe above.
+
+    q: [B, H, N, d], k and v: [B, Hkv, N, d] as torch CPU tensors of the
+    storage dtype; key_lens: int32 [B] or None."""
+    g = torch.Generator("cpu").manual_seed(int(seed))
+    q = torch.randn((B, H, N, d), generator=g, dtype=torch.float32)
+    k = torch.randn((B, Hkv, N, d), generator=g, dtype=torch.float32)
+    v = torch.randn((B, Hkv, N, d), generator=g, dtype=torch.float32)
+    if dtype == "bf16":
+        q, k, v = q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
+    elif dtype != "f32":
+        raise ValueError(f"unknown dtype {dtype!r}")
+    key_lens = None
+    if padded:
+        key_lens = torch.randint(N // 2, N + 1, (B,), generator=g, dtype=torch.int32)
+    return q, k, v, key_lens
+
+
+def make_inputs(w: Workload):
+    """Inputs of a named workload: (q, k, v, key_lens) on the CPU."""
+    return make_qkv(w.B, w.H, w.Hkv, w.N, w.d, w.dtype, w.seed, w.padded)
+
+
+def as_f64(t):
+    """Exact fp64 numpy copy of a CPU tensor (bf16 and fp32 both embed exactly)."""
+    return t.detach().to("cpu", torch.float64).numpy()
