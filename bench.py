@@ -1,0 +1,251 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact tiled attention forward pass on one MI355X.
+
+One step = one forward pass (the whole hot path: Q tile load, K/V tile stream,
+QKᵀ, masks, online softmax, P·V, epilogue) over one batch of a named
+synthetic workload, launched through the C ABI on torch's current stream with
+the inputs already resident in HBM.  Prints ONE JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
+                    [--no-cpu-baseline] [--no-extra]
+
+value = 4·B·H·N²·d / time (TFLOP/s, the metric as written) for the headline
+workload (B=4, H=8, N=1024, d=64, bf16, non-causal).  The three long
+bf16 workloads are timed too and reported under "workloads" with both the
+nominal and the algorithmic (causal: N(N+1)/2 pairs, padded: N·Σkey_len
+pairs) rates and their fraction of the bf16 MFMA peak.
+"""
+
+import argparse
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s (4·B·H·N²·d) and % of bf16 MFMA peak, 1 MI355X"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 matrix, published
+HEADLINE = 2
+
+
+def nominal_flops(w):
+    return 4.0 * w.B * w.H * w.N * w.N * w.d
+
+
+def algorithmic_flops(w, key_lens):
+    """Work the method must do: 4·d flops per admissible (query, key) pair."""
+    if w.causal:
+        pairs = w.B * w.H * w.N * (w.N + 1) / 2
+    elif key_lens is not None:
+        pairs = w.H * w.N * float(sum(int(x) for x in key_lens))
+    else:
+        pairs = w.B * w.H * w.N * w.N
+    return 4.0 * w.d * pairs
+
+
+def algorithmic_bytes(w):
+    """Compulsory HBM bytes of one launch: read Q, K, V once, write O and LSE."""
+    e = 2 if w.dtype == "bf16" else 4
+    return (2 * w.B * w.H * w.N * w.d + 2 * w.B * w.Hkv * w.N * w.d) * e + 4 * w.B * w.H * w.N
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "exact_tiled_attention_14_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload_id):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, or None
+    when they are absent or were taken on another version of the kernels."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    ent = rec.get("workloads", {}).get(str(workload_id))
+    return None if ent is None else ent.get("bytes_per_launch")
+
+
+class Runner:
+    """Inputs of one workload resident on the GPU and a raw C-ABI launch."""
+
+    def __init__(self, w, dev):
+        import torch
+
+        import exact_tiled_attention_14_amd as attn
+        from workloads import make_inputs
+
+        self.w = w
+        q, k, v, kl = make_inputs(w)
+        self.key_lens_host = None if kl is None else kl.tolist()
+        self.q, self.k, self.v = q.to(dev), k.to(dev), v.to(dev)
+        self.kl = None if kl is None else kl.to(dev)
+        self.o = torch.empty_like(self.q)
+        self.lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+        self.stream = torch.cuda.current_stream(dev)
+        self.fn = attn.attn_fwd_bf16 if w.dtype == "bf16" else attn.attn_fwd_f32
+        self.args = (self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), self.o.data_ptr(),
+                     self.lse.data_ptr(), w.B, w.H, w.Hkv, w.N, w.d, w.scale, int(w.causal),
+                     None if self.kl is None else self.kl.data_ptr(), self.stream.cuda_stream)
+
+    def launch(self):
+        st = self.fn(*self.args)
+        if st != 0:
+            raise RuntimeError(f"attention launch failed with status {st}")
+
+    def time(self, steps, warmup):
+        """Average milliseconds per launch over `steps` back-to-back launches,
+        bracketed by HIP events recorded on the launch stream."""
+        import torch
+
+        for _ in range(warmup):
+            self.launch()
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(self.stream)
+        for _ in range(steps):
+            self.launch()
+        end.record(self.stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / steps
+
+
+def cpu_baseline(w, budget_s=10.0):
+    """The fp64 oracle, as it stands, on this host's cores over a bounded sample
+    of the workload: whole (b, h) heads, all query rows, in order, repeating
+    passes over the workload until about ``budget_s`` seconds are spent.
+    Reported in the metric's unit (TFLOP/s of the nominal 4·N²·d count per
+    head)."""
+    import numpy as np
+
+    import oracle
+    from workloads import as_f64, make_inputs
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    q, k, v, kl = make_inputs(w)
+    q, k, v = as_f64(q), as_f64(k), as_f64(v)
+    group = w.H // w.Hkv
+    heads = 0
+    t0 = time.perf_counter()
+    done = False
+    while not done:
+        for b in range(w.B):
+            for h in range(w.H):
+                g = h // group
+                oracle.attention(q[b:b + 1, h:h + 1], k[b:b + 1, g:g + 1], v[b:b + 1, g:g + 1],
+                                 w.scale, causal=w.causal,
+                                 key_lens=None if kl is None else [int(kl[b])])
+                heads += 1
+                if time.perf_counter() - t0 >= budget_s:
+                    done = True
+                    break
+            if done:
+                break
+    dt = time.perf_counter() - t0
+    flops = 4.0 * heads * w.N * w.N * w.d
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{heads} (b,h) head passes ({heads / (w.B * w.H):.2f} x the {w.B * w.H}-head "
+                      f"workload), all {w.N} query rows each, fp64 numpy, {dt:.1f} s wall",
+            "seconds": round(dt, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=HEADLINE)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip timing the other bf16 workloads")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): the forward pass "
+              "has no multi-GPU path; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from workloads import WORKLOADS
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    w = WORKLOADS[args.workload]
+
+    r = Runner(w, dev)
+    ms = r.time(args.steps, args.warmup)
+    nom = nominal_flops(w)
+    alg = algorithmic_flops(w, r.key_lens_host)
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    achieved = alg / (ms * 1e-3) / 1e12
+    traffic = stored_traffic(args.workload)
+
+    line = {
+        "metric": METRIC,
+        "value": round(nom / (ms * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded i.i.d. N(0,1) q/k/v; no dataset)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Hkv": w.Hkv, "N": w.N, "d": w.d,
+                   "causal": w.causal, "padded": w.padded, "scale": w.scale},
+        "frac_of_bf16_peak": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": traffic,
+                     "algorithmic_bytes": algorithmic_bytes(w),
+                     "algorithmic_flops": alg},
+    }
+
+    if not args.no_extra:
+        extra = {}
+        for wid in (3, 4, 5):
+            if wid == args.workload:
+                continue
+            ww = WORKLOADS[wid]
+            rr = Runner(ww, dev)
+            steps = max(10, min(args.steps, 100))
+            m = rr.time(steps, max(3, args.warmup // 4))
+            a = algorithmic_flops(ww, rr.key_lens_host)
+            extra[str(wid)] = {
+                "workload": ww.name, "ms": round(m, 4), "steps": steps,
+                "nominal_tflops": round(nominal_flops(ww) / (m * 1e-3) / 1e12, 2),
+                "algorithmic_tflops": round(a / (m * 1e-3) / 1e12, 2),
+                "frac_of_bf16_peak": round(a / (m * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "traffic": stored_traffic(wid),
+            }
+            del rr
+        line["workloads"] = extra
+
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w)
+
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

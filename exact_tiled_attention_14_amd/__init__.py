@@ -1,0 +1,125 @@
+"""Python binding of the MI355X exact tiled attention forward library.
+
+Thin ctypes layer over ``libattn.so`` (see ``include/attn.h``): the functions
+``attn_fwd_bf16``, ``attn_fwd_f32``, ``attn_fwd`` and ``attn_status_str`` take
+the same arguments as the C entry points (device pointers as Python ints) and
+return the status code.  ``forward`` marshals torch tensors onto them; every
+step of the computation runs in the HIP kernels.  There is no fallback: if
+the library is missing, every call raises.
+"""
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "AttnError", "attn_fwd", "attn_fwd_bf16", "attn_fwd_f32", "attn_status_str",
+    "forward", "library_path", "load_library",
+    "ATTN_OK", "ATTN_ERR_NULL", "ATTN_ERR_SHAPE", "ATTN_ERR_HEAD_DIM", "ATTN_ERR_ALIGN",
+    "ATTN_ERR_SCALE", "ATTN_ERR_HIP",
+]
+
+ATTN_OK, ATTN_ERR_NULL, ATTN_ERR_SHAPE, ATTN_ERR_HEAD_DIM = 0, 1, 2, 3
+ATTN_ERR_ALIGN, ATTN_ERR_SCALE, ATTN_ERR_HIP = 4, 5, 6
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+# (name, argtypes) of every exported entry point, matching include/attn.h
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_FWD_ARGS = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_float, _I, _P, _P]
+ENTRY_POINTS = {
+    "attn_fwd_bf16": (_FWD_ARGS, ctypes.c_int),
+    "attn_fwd_f32": (_FWD_ARGS, ctypes.c_int),
+    "attn_fwd": (_FWD_ARGS, ctypes.c_int),
+    "attn_status_str": ([_I], ctypes.c_char_p),
+}
+
+
+class AttnError(RuntimeError):
+    """A non-zero status from the library."""
+
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({attn_status_str(status)})")
+
+
+def library_path():
+    return os.path.join(_HERE, "libattn.so")
+
+
+def load_library():
+    """Load libattn.so (built by ``exact_tiled_attention_14_amd.build``)."""
+    global _LIB
+    if _LIB is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"{path} is missing: build it first (python -m exact_tiled_attention_14_amd.build); "
+                "there is no fallback implementation")
+        lib = ctypes.CDLL(path)
+        for name, (argtypes, restype) in ENTRY_POINTS.items():
+            fn = getattr(lib, name)
+            fn.argtypes = argtypes
+            fn.restype = restype
+        _LIB = lib
+    return _LIB
+
+
+def attn_fwd_bf16(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, key_lens, stream):
+    return load_library().attn_fwd_bf16(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, key_lens, stream)
+
+
+def attn_fwd_f32(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, key_lens, stream):
+    return load_library().attn_fwd_f32(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, key_lens, stream)
+
+
+def attn_fwd(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, key_lens, stream):
+    return load_library().attn_fwd(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, key_lens, stream)
+
+
+def attn_status_str(status):
+    return load_library().attn_status_str(int(status)).decode()
+
+
+def forward(q, k, v, *, scale=None, causal=False, key_lens=None, out=None, lse=None, stream=None):
+    """Run the forward pass on torch tensors already on the GPU.
+
+    q: [B, H, N, d]; k, v: [B, Hkv, N, d]; all bf16 or all fp32, contiguous.
+    key_lens: None or an int32 CUDA tensor [B].  scale defaults to 1/sqrt(d).
+    Returns (o, lse): o like q, lse fp32 [B, H, N].  The launch is enqueued on
+    ``stream`` (default: torch's current stream of q's device) and not waited on.
+    """
+    import torch
+
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D: [B, H, N, d] and [B, Hkv, N, d]")
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    if tuple(k.shape) != (B, Hkv, N, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("q, k, v must all be bfloat16 or all float32")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if key_lens is not None:
+        if key_lens.dtype != torch.int32 or not key_lens.is_cuda or key_lens.numel() != B:
+            raise ValueError("key_lens must be an int32 GPU tensor with B entries")
+        key_lens = key_lens.contiguous()
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    fn = attn_fwd_bf16 if q.dtype == torch.bfloat16 else attn_fwd_f32
+    st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+            B, H, Hkv, N, d, float(scale), int(bool(causal)),
+            key_lens.data_ptr() if key_lens is not None else None, stream)
+    if st != ATTN_OK:
+        raise AttnError(st, fn.__name__)
+    return out, lse

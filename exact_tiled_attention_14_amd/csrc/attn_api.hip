@@ -1,0 +1,99 @@
+// attn_api.hip — the C ABI declared in include/attn.h: host-side argument
+// validation (no HIP call on an invalid call) and dispatch to the kernels.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/attn.h"
+#include "attn_common.h"
+
+namespace attn {
+hipError_t launch_fwd_bf16(const Params& p, int d, bool causal, hipStream_t stream);
+hipError_t launch_fwd_f32(const Params& p, int d, bool causal, hipStream_t stream);
+}  // namespace attn
+
+namespace {
+
+constexpr int64_t kMaxWorkgroups = (1 << 24) - 1;
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+int validate(const void* q, const void* k, const void* v, const void* o, const void* lse,
+             int B, int H, int Hkv, int N, int d, float scale, int causal,
+             const int32_t* key_lens, attn::Params* p, bool* empty) {
+    if (B < 0 || N < 0 || H < 1 || Hkv < 1 || H % Hkv != 0 || (causal != 0 && causal != 1))
+        return ATTN_ERR_SHAPE;
+    if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
+    if (!isfinite(scale)) return ATTN_ERR_SCALE;
+    const int64_t tiles = ((int64_t)N + attn::kBR - 1) / attn::kBR;
+    if ((int64_t)B * H * tiles > kMaxWorkgroups) return ATTN_ERR_SHAPE;
+    if ((int64_t)B * H * N > ((int64_t)1 << 62) / d) return ATTN_ERR_SHAPE;
+    *empty = (B == 0 || N == 0);
+    if (*empty) return ATTN_OK;
+    if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+        (key_lens && !aligned16(key_lens)))
+        return ATTN_ERR_ALIGN;
+    p->q = q;
+    p->k = k;
+    p->v = v;
+    p->o = const_cast<void*>(o);
+    p->lse = static_cast<float*>(const_cast<void*>(lse));
+    p->key_lens = key_lens;
+    p->B = B;
+    p->H = H;
+    p->Hkv = Hkv;
+    p->N = N;
+    p->q_tiles = (int)tiles;
+    p->scale_log2 = fabsf(scale) * 1.44269504088896340736f;
+    p->negate_q = scale < 0.f;
+    return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int H, int Hkv, int N, int d, float scale, int causal,
+                  const int32_t* key_lens, void* stream) {
+    attn::Params p;
+    bool empty = false;
+    const int st = validate(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, key_lens, &p, &empty);
+    if (st != ATTN_OK || empty) return st;
+    (void)hipGetLastError();
+    const hipError_t e = attn::launch_fwd_bf16(p, d, causal != 0, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                 int B, int H, int Hkv, int N, int d, float scale, int causal,
+                 const int32_t* key_lens, void* stream) {
+    attn::Params p;
+    bool empty = false;
+    const int st = validate(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, key_lens, &p, &empty);
+    if (st != ATTN_OK || empty) return st;
+    (void)hipGetLastError();
+    const hipError_t e = attn::launch_fwd_f32(p, d, causal != 0, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int H, int Hkv, int N, int d, float scale, int causal,
+             const int32_t* key_lens, void* stream) {
+    return attn_fwd_bf16(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, key_lens, stream);
+}
+
+const char* attn_status_str(int status) {
+    switch (status) {
+        case ATTN_OK: return "ok";
+        case ATTN_ERR_NULL: return "a required pointer is NULL";
+        case ATTN_ERR_SHAPE: return "B, H, Hkv, N or causal out of range, or the problem is too large";
+        case ATTN_ERR_HEAD_DIM: return "head dimension d must be 64 or 128";
+        case ATTN_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+        case ATTN_ERR_SCALE: return "scale must be finite";
+        case ATTN_ERR_HIP: return "HIP kernel launch failed";
+        default: return "unknown attn status";
+    }
+}
+
+}  // extern "C"

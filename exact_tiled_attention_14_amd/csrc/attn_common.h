@@ -1,0 +1,89 @@
+// attn_common.h — device helpers shared by the bf16 and fp32 forward kernels.
+//
+// Work decomposition (the query-block-outer, key-block-inner loop of the
+// tiled forward pass: zsdodo.com page "AI训练的最大障碍不是算力,而是“内存墙”",
+// blockwise code block; aiknowledge.cn "第四章 注意力机制实战案例" §4.1.3): one
+// workgroup owns BR = 128 query rows of one (batch, head); each of its four
+// 64-wide waves owns 32 of those rows.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBR = 32 * kWaves;  // query rows per workgroup
+constexpr int kXcds = 8;          // MI355X: 8 accelerator complex dies
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+struct Params {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    const int32_t* key_lens;
+    int B, H, Hkv, N;
+    int q_tiles;        // ceil(N / kBR)
+    float scale_log2;   // |scale| * log2(e): scores are kept in base-2 units
+    int negate_q;       // scale < 0: q is negated in registers and |scale| used
+};
+
+// Workgroup -> (b, h, query tile).  The hardware deals consecutive workgroup
+// ids round-robin over the 8 XCDs (each with its own L2), so logical ids are
+// renumbered to give every XCD one contiguous run of (b, h, tile) work: the
+// query tiles of a head, which all stream that head's K/V, then share one L2.
+// Under a causal mask tiles are issued longest first (load balance, one of the
+// FlashAttention-2 improvements listed in the FlashAttention2 code block of
+// the zsdodo.com page).
+struct Tile {
+    int b, h, tile;
+};
+
+template <bool CAUSAL>
+__device__ inline Tile map_workgroup(const Params& p) {
+    const int G = gridDim.x;
+    const int w = blockIdx.x;
+    const int x = w % kXcds, k = w / kXcds;
+    const int per = G / kXcds, extra = G % kXcds;
+    const int logical = x * per + min(x, extra) + k;
+    const int bh = logical / p.q_tiles;
+    int t = logical - bh * p.q_tiles;
+    if (CAUSAL) t = p.q_tiles - 1 - t;
+    Tile r;
+    r.b = bh / p.H;
+    r.h = bh - r.b * p.H;
+    r.tile = t;
+    return r;
+}
+
+// Number of keys this workgroup must look at: the valid key length of the
+// sequence (padded positions are ignored), cut under a causal mask at the
+// last query row of the tile.
+template <bool CAUSAL>
+__device__ inline int key_limit(const Params& p, int b, int q0, int* kv_len_out) {
+    int kv_len = p.N;
+    if (p.key_lens != nullptr) {
+        const int kl = p.key_lens[b];
+        kv_len = kl < 0 ? 0 : (kl > p.N ? p.N : kl);
+    }
+    *kv_len_out = kv_len;
+    int lim = kv_len;
+    if (CAUSAL) lim = min(lim, min(q0 + kBR, p.N));
+    return lim;
+}
+
+__device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Value of lane (lane ^ 32): the other half-wave, which holds the same query
+// rows for the other half of the keys.
+__device__ inline float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
+
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kLn2 = 0.693147180559945309f;
+
+}  // namespace attn

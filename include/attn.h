@@ -1,0 +1,81 @@
+/*
+ * attn.h — C ABI of the MI355X (gfx950) exact tiled attention forward pass.
+ *
+ * Operation (standard attention of the zsdodo.com page "AI训练的最大障碍不是算力,
+ * 而是“内存墙”", code block of standard PyTorch attention; softmax with the row
+ * max subtracted, unite.ai page "闪电注意力：革命性地提高Transformer效率", section
+ * "闪电注意力的数学原理", formula 1; tiled with a running max m and running sum ℓ as
+ * in the ``safe_softmax_block`` code block of the zsdodo.com page): for batch b,
+ * query head h, query row i, with kv head g = h / (H / Hkv) and admissible keys
+ *     A(b,i) = { j in [0, N) : j < key_len_b  and  (causal == 0 or j <= i) },
+ *     s_ij   = scale * <q[b,h,i,:], k[b,g,j,:]>,
+ *     m_i    = max_{j in A} s_ij,   ℓ_i = sum_{j in A} exp(s_ij - m_i),
+ *     o[b,h,i,:] = sum_{j in A} exp(s_ij - m_i) * v[b,g,j,:] / ℓ_i,
+ *     lse[b,h,i] = m_i + ln ℓ_i   (natural log).
+ * A row with no admissible key (key_len_b == 0) gets o = 0 and lse = -inf.
+ * The N x N score matrix is never written to memory; the library allocates
+ * nothing and needs no workspace.
+ *
+ * Layouts (all contiguous, row-major, element strides implied by the sizes):
+ *     q, o : [B][H][N][d]      k, v : [B][Hkv][N][d]      lse : [B][H][N] fp32
+ *     key_lens : NULL (every sequence has N keys) or int32 [B] in DEVICE memory;
+ *                each value is clamped to [0, N] on the device.
+ * All pointers except key_lens are DEVICE pointers owned by the caller; every
+ * non-NULL pointer must be 16-byte aligned.  o must not overlap q, k or v
+ * (undefined result otherwise).
+ *
+ * Execution: the kernel is enqueued on `stream` (a hipStream_t; NULL = the
+ * null stream) and the call returns without waiting.  Arguments are validated
+ * on the host before any HIP call, so an invalid call touches no device
+ * state.  Calls keep no state and are thread-safe.  No C++ exception crosses
+ * this interface.
+ *
+ * Sizes: B >= 0, N >= 0 (B == 0 or N == 0 is a no-op returning ATTN_OK, and
+ * the data pointers may then be NULL), H >= 1, Hkv >= 1, H % Hkv == 0,
+ * d in {64, 128}, causal in {0, 1}, scale finite; B*H*ceil(N/128) work tiles
+ * must not exceed 16,777,215 and B*H*N*d must stay below 2^62.
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL = 1,      /* a required pointer is NULL                         */
+    ATTN_ERR_SHAPE = 2,     /* B, H, Hkv, N or causal out of range, or too large  */
+    ATTN_ERR_HEAD_DIM = 3,  /* d is not 64 or 128                                 */
+    ATTN_ERR_ALIGN = 4,     /* a pointer is not 16-byte aligned                   */
+    ATTN_ERR_SCALE = 5,     /* scale is NaN or infinite                           */
+    ATTN_ERR_HIP = 6        /* the kernel launch failed (hipGetLastError)         */
+} attn_status;
+
+/* bf16 q, k, v, o (raw 16-bit bfloat16 storage); fp32 lse.  QKᵀ and P·V run on
+ * bf16 matrix cores with fp32 accumulation; the softmax runs in fp32; P is
+ * rounded to bf16 before P·V and o is rounded to bf16 (nearest even). */
+int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int H, int Hkv, int N, int d, float scale, int causal,
+                  const int32_t* key_lens, void* stream);
+
+/* fp32 q, k, v, o and lse; every product and sum in fp32 (fp32 matrix cores). */
+int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                 int B, int H, int Hkv, int N, int d, float scale, int causal,
+                 const int32_t* key_lens, void* stream);
+
+/* The hot path: identical to attn_fwd_bf16. */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int H, int Hkv, int N, int d, float scale, int causal,
+             const int32_t* key_lens, void* stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* attn_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

@@ -1,0 +1,105 @@
+"""The C ABI without a GPU: the library loads, exports every entry point that
+include/*.h declares, and rejects invalid arguments on the host (these calls
+return before any HIP call, so they run on a machine with no GPU)."""
+
+import ctypes
+import glob
+import math
+import os
+import re
+
+import pytest
+
+import exact_tiled_attention_14_amd as attn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = []
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        src = open(h).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_entry_points():
+    assert _declared_functions() == sorted(attn.ENTRY_POINTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = attn.load_library()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    assert attn.attn_status_str(0) == "ok"
+    for s in range(1, 7):
+        assert attn.attn_status_str(s) and attn.attn_status_str(s) != "ok"
+    assert "unknown" in attn.attn_status_str(99)
+
+
+# fake, 16-byte aligned, never dereferenced device addresses
+P = 0x10000
+GOOD = dict(q=P, k=P * 2, v=P * 3, o=P * 4, lse=P * 5, B=1, H=4, Hkv=2, N=64, d=64,
+            scale=0.125, causal=0, key_lens=None, stream=None)
+
+
+def call(fn, **over):
+    a = dict(GOOD, **over)
+    return fn(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"], a["N"], a["d"],
+              a["scale"], a["causal"], a["key_lens"], a["stream"])
+
+
+ENTRY = [attn.attn_fwd_bf16, attn.attn_fwd_f32, attn.attn_fwd]
+
+
+@pytest.mark.parametrize("fn", ENTRY, ids=lambda f: f.__name__)
+@pytest.mark.parametrize("over,status", [
+    (dict(d=96), attn.ATTN_ERR_HEAD_DIM),
+    (dict(d=0), attn.ATTN_ERR_HEAD_DIM),
+    (dict(d=256), attn.ATTN_ERR_HEAD_DIM),
+    (dict(H=3, Hkv=2), attn.ATTN_ERR_SHAPE),
+    (dict(H=0), attn.ATTN_ERR_SHAPE),
+    (dict(Hkv=0), attn.ATTN_ERR_SHAPE),
+    (dict(B=-1), attn.ATTN_ERR_SHAPE),
+    (dict(N=-5), attn.ATTN_ERR_SHAPE),
+    (dict(causal=2), attn.ATTN_ERR_SHAPE),
+    (dict(B=65536, H=256, Hkv=256, N=2**20), attn.ATTN_ERR_SHAPE),
+    (dict(scale=math.nan), attn.ATTN_ERR_SCALE),
+    (dict(scale=math.inf), attn.ATTN_ERR_SCALE),
+    (dict(q=None), attn.ATTN_ERR_NULL),
+    (dict(k=None), attn.ATTN_ERR_NULL),
+    (dict(v=None), attn.ATTN_ERR_NULL),
+    (dict(o=None), attn.ATTN_ERR_NULL),
+    (dict(lse=None), attn.ATTN_ERR_NULL),
+    (dict(q=P + 8), attn.ATTN_ERR_ALIGN),
+    (dict(o=P + 2), attn.ATTN_ERR_ALIGN),
+    (dict(lse=P + 4), attn.ATTN_ERR_ALIGN),
+    (dict(key_lens=P + 4), attn.ATTN_ERR_ALIGN),
+    # empty problems are a no-op and may pass NULL data pointers
+    (dict(B=0, q=None, k=None, v=None, o=None, lse=None), attn.ATTN_OK),
+    (dict(N=0, q=None, k=None, v=None, o=None, lse=None), attn.ATTN_OK),
+])
+def test_host_validation(fn, over, status):
+    assert call(fn, **over) == status
+
+
+def test_python_forward_rejects_bad_tensors():
+    import torch
+    q = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        attn.forward(q, q, q)            # CPU tensors
+    with pytest.raises(ValueError):
+        attn.forward(q[0], q, q)         # wrong rank
+    with pytest.raises(TypeError):
+        attn.forward(q, q.float(), q)    # mixed dtypes
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(attn, "_LIB", None)
+    monkeypatch.setattr(attn, "library_path", lambda: str(tmp_path / "nope.so"))
+    with pytest.raises(RuntimeError, match="no fallback"):
+        attn.load_library()
