@@ -27,6 +27,8 @@ int validate(const void* q, const void* k, const void* v, const void* o, const v
     const int64_t tiles = ((int64_t)N + attn::kBR - 1) / attn::kBR;
     if ((int64_t)B * H * tiles > kMaxWorkgroups) return ATTN_ERR_SHAPE;
     if ((int64_t)B * H * N > ((int64_t)1 << 62) / d) return ATTN_ERR_SHAPE;
+    // one (b, head) slice of q/k/v must be addressable with 32-bit byte offsets
+    if ((int64_t)N * d * 4 >= ((int64_t)1 << 31)) return ATTN_ERR_SHAPE;
     *empty = (B == 0 || N == 0);
     if (*empty) return ATTN_OK;
     if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;

@@ -33,7 +33,10 @@
  * Sizes: B >= 0, N >= 0 (B == 0 or N == 0 is a no-op returning ATTN_OK, and
  * the data pointers may then be NULL), H >= 1, Hkv >= 1, H % Hkv == 0,
  * d in {64, 128}, causal in {0, 1}, scale finite; B*H*ceil(N/128) work tiles
- * must not exceed 16,777,215 and B*H*N*d must stay below 2^62.
+ * must not exceed 16,777,215, N*d*4 must stay below 2^31 (one head's slice is
+ * addressed with 32-bit byte offsets: N <= 4,194,303 at d = 128) and B*H*N*d
+ * below 2^62.  Checks run in this order: shape, head dim, scale, size limits,
+ * empty problem (returns ATTN_OK), NULL pointers, alignment.
  */
 #ifndef ATTN_H
 #define ATTN_H
