@@ -1,5 +1,6 @@
 // attn_api.hip — the C ABI declared in include/attn.h: host-side argument
 // validation (no HIP call on an invalid call) and dispatch to the kernels.
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 
@@ -46,7 +47,9 @@ int validate(const void* q, const void* k, const void* v, const void* o, const v
     p->Hkv = Hkv;
     p->N = N;
     p->q_tiles = (int)tiles;
-    p->scale_log2 = fabsf(scale) * 1.44269504088896340736f;
+    const float c = fabsf(scale) * 1.44269504088896340736f;
+    p->zero_q = !(c >= FLT_MIN);
+    p->scale_log2 = p->zero_q ? 1.0f : c;
     p->negate_q = scale < 0.f;
     return ATTN_OK;
 }

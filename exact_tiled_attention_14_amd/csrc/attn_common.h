@@ -29,8 +29,10 @@ struct Params {
     const int32_t* key_lens;
     int B, H, Hkv, N;
     int q_tiles;        // ceil(N / kBR)
-    float scale_log2;   // |scale| * log2(e): scores are kept in base-2 units
+    float scale_log2;   // c = |scale| * log2(e) > 0: scores are kept in base-2 units
     int negate_q;       // scale < 0: q is negated in registers and |scale| used
+    int zero_q;         // scale == 0 (or |scale|·log2 e below the normal range):
+                        // every score is 0, computed as q = 0 with c = 1
 };
 
 // Workgroup -> (b, h, query tile).  The hardware deals consecutive workgroup

@@ -7,8 +7,7 @@
 //
 //   Sᵀ = K_tile · Qᵀ            v_mfma_f32_32x32x16_bf16, fp32 accumulate
 //   mask (only on tiles that straddle the causal diagonal or the key end)
-//   m' = max(m, rowmax), α = 2^(m−m'), P = 2^(S·c − m'), ℓ' = α·ℓ + ΣP,
-//   Oᵀ ← α·Oᵀ + Vᵀ · Pᵀ          P rounded to bf16, same MFMA
+//   P = 2^(S·c − m), ℓ ← α·ℓ + ΣP, Oᵀ ← α·Oᵀ + Vᵀ · Pᵀ (P rounded to bf16)
 //
 // which is the running-max / running-sum recurrence of the safe_softmax_block
 // code block (zsdodo.com page "AI训练的最大障碍不是算力,而是“内存墙”") with the
@@ -16,52 +15,110 @@
 // base 2 with c = |scale|·log2(e).  The epilogue divides by ℓ once and writes
 // O (bf16) and LSE = (m + log2 ℓ)·ln 2 (fp32).
 //
-// The running max is only moved when a tile's max exceeds it by more than
-// kRescaleSlack (in log2 units).  Any reference value m gives the same O/ℓ
-// and m + log2 ℓ, the definition's values, as long as nothing overflows; with
-// the slack P stays ≤ 2^kRescaleSlack, and most tiles skip the α·Oᵀ rescale.
-// ℓ sums the fp32 P (summing the bf16-rounded P would move LSE by up to
-// 2^-9 on short rows).
+// Reference value m.  O/ℓ and m + log2 ℓ equal the definition's values for
+// ANY reference m, provided no exponent overflows; the row max is simply the
+// safe choice.  Here m is set to the exact running max on a wave's first tile
+// and on every masked tile (α = 2^(m_old − m_new) rescales ℓ and Oᵀ there, as
+// in safe_softmax_block); on the other tiles the old m is kept and the tile
+// is accepted if its per-lane sum of P stays below 2^20 — every P, and hence
+// ℓ and Oᵀ, is then far from overflow.  A tile that fails the check is redone
+// with the exact max update.  The common case thus costs no max reduction and
+// no rescale.  ℓ sums the fp32 P (summing the bf16-rounded P would move LSE by
+// up to 2^-9 on short rows).
 //
-// Register layouts.  The MFMA computes Sᵀ (keys × queries) so that a lane
-// owns ONE query row (lane % 32) and 16 keys of every 32-key block: the row
-// max and row sum are in-lane reductions plus a single exchange with lane^32.
-// K rows are read in a permuted order so that half-wave h, accumulator r of
-// a 32-key block holds key 16h + r; then the same registers, rounded to bf16,
-// are directly the B operand (keys 16h + 8c .. 16h + 8c + 7) of Oᵀ = Vᵀ·Pᵀ.
-// V is stored transposed in LDS (Vᵀ[d][key]) so that operand is one 16-byte
-// LDS read.  Both LDS tiles are XOR-swizzled on 16-byte chunks against bank
-// conflicts.
+// Register layouts.  The MFMA computes Sᵀ (keys × queries) so that a lane owns
+// ONE query row (lane % 32) and 16 keys of every 32-key block — MFMA output
+// row 8a + 4h + b (a < 4, b < 4) sits in register 4a + b of half-wave h — so
+// row sums are in-lane plus one exchange with lane ^ 32.  Rounded to bf16, the
+// registers 8c .. 8c + 7 of a block are directly the B operand of Oᵀ = Vᵀ·Pᵀ
+// for the 16 keys 16c + {4h .. 4h + 3, 8 + 4h .. 8 + 4h + 3}; Vᵀ is stored in
+// LDS with exactly those 8 keys in one 16-byte chunk, so the A operand is one
+// ds_read_b128.  K rows are padded (d = 128) or XOR-swizzled (d = 64) and the
+// Vᵀ chunks XOR-swizzled so that the MFMA operand reads are bank-conflict
+// free.
 #include "attn_common.h"
 
 namespace attn {
 namespace {
 
-constexpr float kRescaleSlack = 8.0f;
-
-// ---- K tile: LDS [BC][D] bf16, 16-byte chunk (row, c) stored at chunk
-// c ^ kswz(row).  The 8 rows read together by lanes 8m..8m+7 (permuted rows
-// below) get 8 different swizzles.
-__device__ inline int kswz(int row) { return (row & 3) | (((row >> 4) & 1) << 2); }
-
-// Row of a 32-key block read by MFMA row rho: accumulator register r of
-// half-wave h then corresponds to key 16h + r.
-__device__ inline int perm_row(int rho) {
-    return (((rho >> 2) & 1) << 4) | (((rho >> 3) & 3) << 2) | (rho & 3);
-}
-
-// ---- V tile: LDS Vᵀ [D][BC] bf16, chunk of 8 keys (d, c) at c ^ vswz(d).
-__device__ inline int vswz(int d) { return (d ^ (d >> 3)) & 7; }
+constexpr float kSumLimit = 1048576.0f;  // 2^20: per-lane sum of P accepted without a new max
 
 template <int D>
-struct Cfg {
-    static constexpr int BC = 8192 / D;          // keys per tile
-    static constexpr int KBLK = BC / 32;         // 32-key MFMA blocks per tile
-    static constexpr int DCH = D / 16;           // 16-wide d chunks (MFMA k steps)
-    static constexpr int DBLK = D / 32;          // 32-row blocks of Oᵀ
-    static constexpr int TILE_BYTES = BC * D * 2;  // 16 KiB
-    static constexpr int STAGE_BYTES = 2 * TILE_BYTES;  // K + V
-    static constexpr int CPR = D / 8;            // 16-byte chunks per K row
+struct Cfg;
+
+template <>
+struct Cfg<128> {
+    static constexpr int BC = 64;
+    static constexpr int KROW = 128 * 2 + 16;  // padded K row
+    static constexpr int VROW = BC * 2;
+    static constexpr int K_BYTES = BC * KROW;
+    static constexpr int V_BYTES = 128 * VROW;
+    // byte offset of 16-byte chunk `ch` of K row `row` in the K tile
+    __device__ static int kpos(int row, int ch) { return row * KROW + ch * 16; }
+    // byte offset of key-chunk P of Vᵀ row d in the Vᵀ tile
+    __device__ static int vpos(int d, int P) {
+        const int x = d & 31;
+        return d * VROW + ((P ^ ((x ^ (x >> 3)) & 7)) << 4);
+    }
+};
+
+template <>
+struct Cfg<64> {
+    static constexpr int BC = 128;
+    static constexpr int KROW = 64 * 2;  // XOR-swizzled K row
+    static constexpr int VROW = BC * 2;
+    static constexpr int K_BYTES = BC * KROW;
+    static constexpr int V_BYTES = 64 * VROW;
+    __device__ static int kpos(int row, int ch) { return row * KROW + ((ch ^ ((row >> 1) & 7)) << 4); }
+    __device__ static int vpos(int d, int P) {
+        const int x = d & 31;
+        return d * VROW + ((P ^ ((x ^ (x >> 2)) & 15)) << 4);
+    }
+};
+
+template <int D>
+struct Geo {
+    using L = Cfg<D>;
+    static constexpr int BC = L::BC;
+    static constexpr int KBLK = BC / 32;   // 32-key MFMA blocks per tile
+    static constexpr int DCH = D / 16;     // 16-wide d chunks (Sᵀ k steps)
+    static constexpr int DBLK = D / 32;    // 32-row blocks of Oᵀ
+    static constexpr int CPR = D / 8;      // 16-byte chunks per K row
+    static constexpr int STAGE = L::K_BYTES + L::V_BYTES;
+};
+
+// Per-thread byte offsets, fixed for the whole kernel.  Offsets that differ
+// between a thread's accesses only by a compile-time constant are kept once.
+template <int D>
+struct Offsets {
+    using G = Geo<D>;
+    using L = Cfg<D>;
+    // K chunk i of a thread: idx = tid + 256 i, i.e. row + i·(256/CPR), same column
+    static constexpr int KROWS_PER_PASS = kThreads / G::CPR;
+    uint32_t k_ld;                     // global, first K chunk of this thread (tile-relative)
+    uint32_t k_st;                     // LDS, first K chunk of this thread
+    uint32_t v_ld;                     // global, first V key of this thread (tile-relative)
+    uint32_t v_st[4];                  // LDS, Vᵀ rows d0 .. d0+3 (relative to the V tile)
+    uint32_t k_rd[G::DCH];             // LDS, Sᵀ A operand, key block 0
+    uint32_t v_rd[G::KBLK][2];         // LDS, Oᵀ A operand, d block 0 (relative to the V tile)
+
+    __device__ inline void init(int tid, int hl, int ql) {
+        const int row = tid / G::CPR, ch = tid % G::CPR;
+        k_ld = (uint32_t)(row * D * 2 + ch * 16);
+        k_st = (uint32_t)L::kpos(row, ch);  // the swizzle ignores row bits >= 4
+        // Vᵀ chunk P of this thread holds keys 16(P>>1) + 4(P&1) + {0..3, 8..11}
+        const int P = tid / (D / 4), d4 = tid % (D / 4);
+        const int key0 = 16 * (P >> 1) + 4 * (P & 1);
+        v_ld = (uint32_t)(key0 * D * 2 + d4 * 8);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v_st[j] = (uint32_t)L::vpos(4 * d4 + j, P);
+#pragma unroll
+        for (int c = 0; c < G::DCH; ++c) k_rd[c] = (uint32_t)L::kpos(ql, 2 * c + hl);
+#pragma unroll
+        for (int blk = 0; blk < G::KBLK; ++blk)
+#pragma unroll
+            for (int c = 0; c < 2; ++c) v_rd[blk][c] = (uint32_t)L::vpos(ql, blk * 4 + c * 2 + hl);
+    }
 };
 
 template <int D>
@@ -70,74 +127,30 @@ struct KVRegs {
     uint2 v[8];  // 8 keys x 4 d of V per thread (for the transposed store)
 };
 
-// Per-thread byte offsets, fixed for the whole kernel.
-template <int D>
-struct Lanes {
-    uint32_t kg_off[4];   // global offset of this thread's K chunks within a tile
-    uint32_t vg_off;      // global offset of this thread's first V key within a tile
-    uint32_t ks_off[4];   // LDS offset of this thread's K chunks
-    uint32_t vs_off[4];   // LDS offset (within the V tile) of this thread's Vᵀ rows
-    uint32_t kr_off[Cfg<D>::KBLK][Cfg<D>::DCH];  // LDS reads of the Sᵀ A operand
-    uint32_t vr_off[Cfg<D>::DBLK][Cfg<D>::KBLK][2];  // LDS reads of the Oᵀ A operand
-
-    __device__ inline void init(int tid, int hl, int ql) {
-        using C = Cfg<D>;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int idx = tid + kThreads * i;
-            const int row = idx / C::CPR, ch = idx % C::CPR;
-            kg_off[i] = (uint32_t)(row * D * 2 + ch * 16);
-            ks_off[i] = (uint32_t)(row * D * 2 + ((ch ^ kswz(row)) << 4));
-        }
-        const int kg = tid / (D / 4), d4 = tid % (D / 4);
-        vg_off = (uint32_t)(kg * 8 * D * 2 + d4 * 8);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int d = d4 * 4 + j;
-            vs_off[j] = (uint32_t)(d * (C::BC * 2) + ((kg ^ vswz(d)) << 4));
-        }
-#pragma unroll
-        for (int blk = 0; blk < C::KBLK; ++blk) {
-            const int row = blk * 32 + perm_row(ql);
-#pragma unroll
-            for (int c = 0; c < C::DCH; ++c)
-                kr_off[blk][c] = (uint32_t)(row * D * 2 + (((2 * c + hl) ^ kswz(row)) << 4));
-        }
-#pragma unroll
-        for (int db = 0; db < C::DBLK; ++db) {
-            const int d = db * 32 + ql;
-#pragma unroll
-            for (int blk = 0; blk < C::KBLK; ++blk)
-#pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    const int chunk = blk * 4 + hl * 2 + c;
-                    vr_off[db][blk][c] = (uint32_t)(d * (C::BC * 2) + ((chunk ^ vswz(d)) << 4));
-                }
-        }
-    }
-};
-
 // Global -> registers for the tile starting at key kv0.  The buffer
 // descriptors end at the last valid key (padding and the sequence end), so
 // loads past it return zeros: NaN or any other content there can never reach
 // the output (0 · NaN would otherwise be NaN).
 template <int D>
-__device__ inline void load_kv(KVRegs<D>& r, const Lanes<D>& L, __amdgpu_buffer_rsrc_t kres,
+__device__ inline void load_kv(KVRegs<D>& r, const Offsets<D>& o, __amdgpu_buffer_rsrc_t kres,
                                __amdgpu_buffer_rsrc_t vres, int kv0) {
     const uint32_t base = (uint32_t)kv0 * (D * 2);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r.k[i] = buf_load16(kres, base + L.kg_off[i]);
+    for (int i = 0; i < 4; ++i)
+        r.k[i] = buf_load16(kres, base + o.k_ld + i * Offsets<D>::KROWS_PER_PASS * (D * 2));
 #pragma unroll
-    for (int i = 0; i < 8; ++i) r.v[i] = buf_load8(vres, base + L.vg_off + i * (D * 2));
+    for (int s = 0; s < 8; ++s) r.v[s] = buf_load8(vres, base + o.v_ld + ((s & 3) + 8 * (s >> 2)) * (D * 2));
 }
 
-// Registers -> LDS stage: K row-major (swizzled), V transposed (swizzled).
+// Registers -> LDS stage: K rows, and V transposed into key chunks.
 template <int D>
-__device__ inline void store_kv(const KVRegs<D>& r, const Lanes<D>& L, char* stage) {
-    char* vs = stage + Cfg<D>::TILE_BYTES;
+__device__ inline void store_kv(const KVRegs<D>& r, const Offsets<D>& o, char* stage) {
+    char* vs = stage + Cfg<D>::K_BYTES;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(stage + L.ks_off[i]) = r.k[i];
-    // r.v[i] = {V[key i][d0], V[key i][d0+1]}, {V[key i][d0+2], V[key i][d0+3]}
+    for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<uint4*>(stage + o.k_st + i * Offsets<D>::KROWS_PER_PASS * Cfg<D>::KROW) = r.k[i];
+    // r.v[s] = {V[key s][d0], V[key s][d0+1]}, {V[key s][d0+2], V[key s][d0+3]};
+    // row d0 + j of Vᵀ gets the 8 keys' element j, two keys per dword.
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         uint32_t w[4];
@@ -145,25 +158,115 @@ __device__ inline void store_kv(const KVRegs<D>& r, const Lanes<D>& L, char* sta
         for (int pr = 0; pr < 4; ++pr) {
             const uint32_t a = (j < 2) ? r.v[2 * pr].x : r.v[2 * pr].y;
             const uint32_t b = (j < 2) ? r.v[2 * pr + 1].x : r.v[2 * pr + 1].y;
-            w[pr] = (j & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+            // low half from key 2pr, high half from key 2pr + 1
+            w[pr] = __builtin_amdgcn_perm(b, a, (j & 1) ? 0x07060302u : 0x05040100u);
         }
-        *reinterpret_cast<uint4*>(vs + L.vs_off[j]) = make_uint4(w[0], w[1], w[2], w[3]);
+        *reinterpret_cast<uint4*>(vs + o.v_st[j]) = make_uint4(w[0], w[1], w[2], w[3]);
     }
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
 __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
-    const __bf16 a = (__bf16)lo, b = (__bf16)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    const f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// max / sum of x over the lane pair (lane, lane ^ 32): v_permlane32_swap hands
+// each lane its partner's value in one of the two results, itself in the other.
+__device__ inline float pair_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float pair_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int D>
+struct WaveState {
+    f32x16 acc[Geo<D>::DBLK];
+    float m_run;  // reference max, base-2 scaled units (−∞ before the first tile)
+    float l_run;  // running sum over this lane's keys
+};
+
+// P = 2^(S·c − m) into bf16 pairs; returns this lane's sum of the fp32 P.
+// Masked scores are −∞ and c > 0, so they give P = 0.
+template <int D>
+__device__ inline float exponentiate(const f32x16 (&s)[Geo<D>::KBLK], uint32_t (&pb)[Geo<D>::KBLK][8],
+                                     float c2, float m_use) {
+    float l0 = 0.f, l1 = 0.f;
+#pragma unroll
+    for (int blk = 0; blk < Geo<D>::KBLK; ++blk)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+            const float e0 = exp2_fast(__builtin_fmaf(s[blk][r], c2, -m_use));
+            const float e1 = exp2_fast(__builtin_fmaf(s[blk][r + 1], c2, -m_use));
+            pb[blk][r >> 1] = pack_bf16x2(e0, e1);
+            if (r & 2) l1 += e0 + e1;
+            else l0 += e0 + e1;
+        }
+    return l0 + l1;
+}
+
+// Inadmissible keys of a tile (past the valid key length, or after the query
+// row under a causal mask) get score −∞.
+template <int D, bool CAUSAL>
+__device__ inline void apply_mask(f32x16 (&s)[Geo<D>::KBLK], int kv0, int kv_len, int qrow, int hl) {
+#pragma unroll
+    for (int blk = 0; blk < Geo<D>::KBLK; ++blk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int key = kv0 + blk * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+            const bool ok = key < kv_len && (!CAUSAL || key <= qrow);
+            s[blk][r] = ok ? s[blk][r] : kNegInf;
+        }
+}
+
+// One tile of the online softmax: P (bf16 pairs) and the ℓ / Oᵀ / m update.
+// `exact` (wave-uniform) asks for the running-max update of safe_softmax_block;
+// otherwise the reference max is kept unless the overflow check fails, in
+// which case the tile is redone exactly.
+template <int D>
+__device__ inline void softmax_tile(const f32x16 (&s)[Geo<D>::KBLK], uint32_t (&pb)[Geo<D>::KBLK][8],
+                                    WaveState<D>& w, float c2, bool exact) {
+    float m_new = w.m_run, m_use = w.m_run, lsum;
+    for (;;) {
+        if (exact) {
+            float mx = kNegInf;
+#pragma unroll
+            for (int blk = 0; blk < Geo<D>::KBLK; ++blk)
+#pragma unroll
+                for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[blk][r], s[blk][r + 1]));
+            m_new = fmaxf(w.m_run, pair_max(mx) * c2);
+            m_use = (m_new == kNegInf) ? 0.f : m_new;
+        }
+        lsum = exponentiate<D>(s, pb, c2, m_use);
+        if (exact || __builtin_amdgcn_ballot_w64(lsum > kSumLimit) == 0) break;
+        exact = true;
+    }
+    if (exact) {
+        const float alpha = exp2_fast(w.m_run - m_use);
+        w.m_run = m_new;
+        w.l_run = w.l_run * alpha + lsum;
+#pragma unroll
+        for (int i = 0; i < Geo<D>::DBLK; ++i) w.acc[i] *= alpha;
+    } else {
+        w.l_run += lsum;
+    }
 }
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(Params p) {
-    using C = Cfg<D>;
-    constexpr int BC = C::BC;
-    __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE_BYTES];
+    using G = Geo<D>;
+    using L = Cfg<D>;
+    constexpr int BC = G::BC;
+    __shared__ __attribute__((aligned(16))) char smem[2 * G::STAGE];
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
     const int hl = lane >> 5, ql = lane & 31;
 
     const Tile t = map_workgroup<CAUSAL>(p);
@@ -182,149 +285,105 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(Params p) {
     const __amdgpu_buffer_rsrc_t kres = make_rsrc(kb, (uint32_t)kv_len * (D * 2));
     const __amdgpu_buffer_rsrc_t vres = make_rsrc(vb, (uint32_t)kv_len * (D * 2));
 
-    // Q rows of this lane as the B operand: chunk c holds d = 16c + 8h .. +7.
-    bf16x8 qf[C::DCH];
+    // Q rows of this lane as the Sᵀ B operand: chunk c holds d = 16c + 8h .. +7.
+    bf16x8 qf[G::DCH];
     {
         const __amdgpu_buffer_rsrc_t qres = make_rsrc(qp, (uint32_t)p.N * (D * 2));
         const uint32_t flip = p.negate_q ? 0x80008000u : 0u;
+        const uint32_t keep = p.zero_q ? 0u : 0xffffffffu;
 #pragma unroll
-        for (int c = 0; c < C::DCH; ++c) {
+        for (int c = 0; c < G::DCH; ++c) {
             uint4 u = buf_load16(qres, (uint32_t)qrow * (D * 2) + c * 32 + hl * 16);
-            u.x ^= flip; u.y ^= flip; u.z ^= flip; u.w ^= flip;
+            u.x = (u.x ^ flip) & keep; u.y = (u.y ^ flip) & keep;
+            u.z = (u.z ^ flip) & keep; u.w = (u.w ^ flip) & keep;
             qf[c] = __builtin_bit_cast(bf16x8, u);
         }
     }
 
-    Lanes<D> L;
-    L.init(tid, hl, ql);
+    Offsets<D> o;
+    o.init(tid, hl, ql);
 
-    f32x16 acc[C::DBLK];
+    WaveState<D> w;
 #pragma unroll
-    for (int i = 0; i < C::DBLK; ++i)
+    for (int i = 0; i < G::DBLK; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
-    float m_run = kNegInf;  // reference max, base-2 scaled units
-    float l_run = 0.f;      // running sum (this half-wave's keys)
+        for (int r = 0; r < 16; ++r) w.acc[i][r] = 0.f;
+    w.m_run = kNegInf;
+    w.l_run = 0.f;
+    bool have_ref = false;  // wave-uniform: a reference max has been set
     const float c2 = p.scale_log2;
 
     KVRegs<D> pre;
-    if (ntiles > 0) load_kv<D>(pre, L, kres, vres, 0);
+    if (ntiles > 0) load_kv<D>(pre, o, kres, vres, 0);
 
-    for (int it = 0; it < ntiles; ++it) {
-        char* stage = smem + (it & 1) * C::STAGE_BYTES;
-        store_kv<D>(pre, L, stage);
+    auto step = [&](auto stage_tag, int it) {
+        constexpr int ST = decltype(stage_tag)::value;
+        char* stage = smem + ST * G::STAGE;
+        store_kv<D>(pre, o, stage);
         __syncthreads();
         const int kv0 = it * BC;
-        if (it + 1 < ntiles) load_kv<D>(pre, L, kres, vres, kv0 + BC);
-
+        if (it + 1 < ntiles) load_kv<D>(pre, o, kres, vres, kv0 + BC);
         // Under a causal mask a wave whose rows all precede the tile skips it.
-        if (CAUSAL && kv0 > q0w + 31) continue;
-
-        const char* vs = stage + C::TILE_BYTES;
+        if (CAUSAL && kv0 > q0w + 31) return;
 
         // ---- Sᵀ = K · Qᵀ
-        f32x16 s[C::KBLK];
+        f32x16 s[G::KBLK];
 #pragma unroll
-        for (int blk = 0; blk < C::KBLK; ++blk) {
+        for (int blk = 0; blk < G::KBLK; ++blk) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[blk][r] = 0.f;
 #pragma unroll
-            for (int c = 0; c < C::DCH; ++c) {
-                const uint4 a = *reinterpret_cast<const uint4*>(stage + L.kr_off[blk][c]);
+            for (int c = 0; c < G::DCH; ++c) {
+                const uint4 a = *reinterpret_cast<const uint4*>(stage + o.k_rd[c] + blk * 32 * L::KROW);
                 s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[c],
                                                                  s[blk], 0, 0, 0);
             }
         }
 
-        // ---- mask + tile max (scaled units)
-        const bool need_mask = (kv0 + BC > kv_len) || (CAUSAL && kv0 + BC - 1 > q0w);
-        float mt;
-        if (need_mask) {
-            float mx = kNegInf;
-#pragma unroll
-            for (int blk = 0; blk < C::KBLK; ++blk)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = kv0 + blk * 32 + hl * 16 + r;
-                    const bool ok = key < kv_len && (!CAUSAL || key <= qrow);
-                    const float v = ok ? s[blk][r] * c2 : kNegInf;
-                    s[blk][r] = v;
-                    mx = fmaxf(mx, v);
-                }
-            mt = mx;
-        } else {
-            float mx = kNegInf;
-#pragma unroll
-            for (int blk = 0; blk < C::KBLK; ++blk)
-#pragma unroll
-                for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[blk][r], s[blk][r + 1]));
-            mt = mx * c2;
-        }
-        mt = fmaxf(mt, swap_halves(mt));
-
-        // ---- move the reference max only when the tile exceeds it by the slack
-        const bool grow = mt > m_run + kRescaleSlack;
-        const float alpha = grow ? exp2_fast(m_run - mt) : 1.0f;
-        if (grow) m_run = mt;
-        const float m_use = (m_run == kNegInf) ? 0.f : m_run;
-
-        // ---- P = 2^(S·c − m), bf16 operand, row sum of the rounded P
-        uint32_t pb[C::KBLK][8];
-        float lsum0 = 0.f, lsum1 = 0.f;
-#pragma unroll
-        for (int blk = 0; blk < C::KBLK; ++blk)
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                float e0, e1;
-                if (need_mask) {
-                    e0 = exp2_fast(s[blk][r] - m_use);
-                    e1 = exp2_fast(s[blk][r + 1] - m_use);
-                } else {
-                    e0 = exp2_fast(__builtin_fmaf(s[blk][r], c2, -m_use));
-                    e1 = exp2_fast(__builtin_fmaf(s[blk][r + 1], c2, -m_use));
-                }
-                pb[blk][r >> 1] = pack_bf16x2(e0, e1);
-                if (r & 2) lsum1 += e0 + e1;
-                else lsum0 += e0 + e1;
-            }
-        l_run = l_run * alpha + (lsum0 + lsum1);
-        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-#pragma unroll
-            for (int i = 0; i < C::DBLK; ++i) acc[i] *= alpha;
-        }
+        // ---- softmax
+        uint32_t pb[G::KBLK][8];
+        const bool masked = (kv0 + BC > kv_len) || (CAUSAL && kv0 + BC - 1 > q0w);
+        if (masked) apply_mask<D, CAUSAL>(s, kv0, kv_len, qrow, hl);
+        softmax_tile<D>(s, pb, w, c2, masked || !have_ref);
+        have_ref = true;
 
         // ---- Oᵀ += Vᵀ · Pᵀ
+        const char* vs = stage + L::K_BYTES;
 #pragma unroll
-        for (int db = 0; db < C::DBLK; ++db) {
+        for (int db = 0; db < G::DBLK; ++db)
 #pragma unroll
-            for (int blk = 0; blk < C::KBLK; ++blk)
+            for (int blk = 0; blk < G::KBLK; ++blk)
 #pragma unroll
                 for (int c = 0; c < 2; ++c) {
-                    const uint4 a = *reinterpret_cast<const uint4*>(vs + L.vr_off[db][blk][c]);
+                    const uint4 a = *reinterpret_cast<const uint4*>(vs + o.v_rd[blk][c] + db * 32 * L::VROW);
                     const uint4 b = make_uint4(pb[blk][4 * c], pb[blk][4 * c + 1], pb[blk][4 * c + 2],
                                                pb[blk][4 * c + 3]);
-                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), acc[db], 0, 0, 0);
+                    w.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), w.acc[db], 0, 0, 0);
                 }
-        }
+    };
+
+    for (int it = 0; it < ntiles; it += 2) {
+        step(std::integral_constant<int, 0>{}, it);
+        if (it + 1 < ntiles) step(std::integral_constant<int, 1>{}, it + 1);
     }
 
     // ---- epilogue: O = Oᵀ/ℓ -> bf16, LSE
-    const float l_tot = l_run + swap_halves(l_run);
+    const float l_tot = pair_sum(w.l_run);
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
     if (qrow < p.N) {
         uint16_t* op = static_cast<uint16_t*>(p.o) + ((size_t)(t.b * p.H + t.h) * p.N + qrow) * D;
 #pragma unroll
-        for (int db = 0; db < C::DBLK; ++db)
+        for (int db = 0; db < G::DBLK; ++db)
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
-                uint2 w;
-                w.x = pack_bf16x2(acc[db][4 * a] * inv, acc[db][4 * a + 1] * inv);
-                w.y = pack_bf16x2(acc[db][4 * a + 2] * inv, acc[db][4 * a + 3] * inv);
-                *reinterpret_cast<uint2*>(op + db * 32 + a * 8 + hl * 4) = w;
+                uint2 v;
+                v.x = pack_bf16x2(w.acc[db][4 * a] * inv, w.acc[db][4 * a + 1] * inv);
+                v.y = pack_bf16x2(w.acc[db][4 * a + 2] * inv, w.acc[db][4 * a + 3] * inv);
+                *reinterpret_cast<uint2*>(op + db * 32 + a * 8 + hl * 4) = v;
             }
         if (hl == 0) {
-            const float lse = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : kNegInf;
+            const float lse = l_tot > 0.f ? (w.m_run + log2f(l_tot)) * kLn2 : kNegInf;
             p.lse[(size_t)(t.b * p.H + t.h) * p.N + qrow] = lse;
         }
     }

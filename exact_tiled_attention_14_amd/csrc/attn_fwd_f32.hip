@@ -60,7 +60,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(Params p) {
     // Qᵀ operand: register c holds q[qrow][2c + h]
     float qf[D / 2];
     {
-        const float sgn = p.negate_q ? -1.f : 1.f;
+        const float sgn = p.zero_q ? 0.f : (p.negate_q ? -1.f : 1.f);
 #pragma unroll
         for (int c = 0; c < D / 2; ++c) qf[c] = qrow < p.N ? sgn * qp[(size_t)qrow * D + 2 * c + hl] : 0.f;
     }
