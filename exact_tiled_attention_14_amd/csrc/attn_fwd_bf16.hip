@@ -191,22 +191,18 @@ struct WaveState {
     float l_run;  // running sum over this lane's keys
 };
 
-// P = 2^(S·c − m) into bf16 pairs; returns this lane's sum of the fp32 P.
-// Masked scores are −∞ and c > 0, so they give P = 0.
-template <int D>
-__device__ inline float exponentiate(const f32x16 (&s)[Geo<D>::KBLK], uint32_t (&pb)[Geo<D>::KBLK][8],
-                                     float c2, float m_use) {
+// P = 2^(S·c − m) of one 32-key block into bf16 pairs; returns this lane's
+// sum of the fp32 P.  Masked scores are −∞ and c > 0, so they give P = 0.
+__device__ inline float exponentiate(const f32x16& s, uint32_t (&pb)[8], float c2, float m_use) {
     float l0 = 0.f, l1 = 0.f;
 #pragma unroll
-    for (int blk = 0; blk < Geo<D>::KBLK; ++blk)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-            const float e0 = exp2_fast(__builtin_fmaf(s[blk][r], c2, -m_use));
-            const float e1 = exp2_fast(__builtin_fmaf(s[blk][r + 1], c2, -m_use));
-            pb[blk][r >> 1] = pack_bf16x2(e0, e1);
-            if (r & 2) l1 += e0 + e1;
-            else l0 += e0 + e1;
-        }
+    for (int r = 0; r < 16; r += 2) {
+        const float e0 = exp2_fast(__builtin_fmaf(s[r], c2, -m_use));
+        const float e1 = exp2_fast(__builtin_fmaf(s[r + 1], c2, -m_use));
+        pb[r >> 1] = pack_bf16x2(e0, e1);
+        if (r & 2) l1 += e0 + e1;
+        else l0 += e0 + e1;
+    }
     return l0 + l1;
 }
 
@@ -224,25 +220,22 @@ __device__ inline void apply_mask(f32x16 (&s)[Geo<D>::KBLK], int kv0, int kv_len
         }
 }
 
-// One tile of the online softmax: P (bf16 pairs) and the ℓ / Oᵀ / m update.
-// `exact` (wave-uniform) asks for the running-max update of safe_softmax_block;
-// otherwise the reference max is kept unless the overflow check fails, in
-// which case the tile is redone exactly.
+// One 32-key block of the online softmax: P (bf16 pairs) and the ℓ / Oᵀ / m
+// update.  `exact` (wave-uniform) asks for the running-max update of
+// safe_softmax_block; otherwise the reference max is kept unless the overflow
+// check fails, in which case the block is redone exactly.
 template <int D>
-__device__ inline void softmax_tile(const f32x16 (&s)[Geo<D>::KBLK], uint32_t (&pb)[Geo<D>::KBLK][8],
-                                    WaveState<D>& w, float c2, bool exact) {
+__device__ inline void softmax_block(const f32x16& s, uint32_t (&pb)[8], WaveState<D>& w, float c2, bool exact) {
     float m_new = w.m_run, m_use = w.m_run, lsum;
     for (;;) {
         if (exact) {
             float mx = kNegInf;
 #pragma unroll
-            for (int blk = 0; blk < Geo<D>::KBLK; ++blk)
-#pragma unroll
-                for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[blk][r], s[blk][r + 1]));
+            for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[r], s[r + 1]));
             m_new = fmaxf(w.m_run, pair_max(mx) * c2);
             m_use = (m_new == kNegInf) ? 0.f : m_new;
         }
-        lsum = exponentiate<D>(s, pb, c2, m_use);
+        lsum = exponentiate(s, pb, c2, m_use);
         if (exact || __builtin_amdgcn_ballot_w64(lsum > kSumLimit) == 0) break;
         exact = true;
     }
@@ -340,27 +333,25 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(Params p) {
             }
         }
 
-        // ---- softmax
-        uint32_t pb[G::KBLK][8];
+        // ---- online softmax and Oᵀ += Vᵀ · Pᵀ, one 32-key block at a time
         const bool masked = (kv0 + BC > kv_len) || (CAUSAL && kv0 + BC - 1 > q0w);
         if (masked) apply_mask<D, CAUSAL>(s, kv0, kv_len, qrow, hl);
-        softmax_tile<D>(s, pb, w, c2, masked || !have_ref);
-        have_ref = true;
-
-        // ---- Oᵀ += Vᵀ · Pᵀ
         const char* vs = stage + L::K_BYTES;
 #pragma unroll
-        for (int db = 0; db < G::DBLK; ++db)
+        for (int blk = 0; blk < G::KBLK; ++blk) {
+            uint32_t pb[8];
+            softmax_block<D>(s[blk], pb, w, c2, masked || !have_ref);
+            have_ref = true;
 #pragma unroll
-            for (int blk = 0; blk < G::KBLK; ++blk)
+            for (int db = 0; db < G::DBLK; ++db)
 #pragma unroll
                 for (int c = 0; c < 2; ++c) {
                     const uint4 a = *reinterpret_cast<const uint4*>(vs + o.v_rd[blk][c] + db * 32 * L::VROW);
-                    const uint4 b = make_uint4(pb[blk][4 * c], pb[blk][4 * c + 1], pb[blk][4 * c + 2],
-                                               pb[blk][4 * c + 3]);
+                    const uint4 b = make_uint4(pb[4 * c], pb[4 * c + 1], pb[4 * c + 2], pb[4 * c + 3]);
                     w.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                         __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), w.acc[db], 0, 0, 0);
                 }
+        }
     };
 
     for (int it = 0; it < ntiles; it += 2) {
