@@ -17,13 +17,15 @@
 //
 // Reference value m.  O/ℓ and m + log2 ℓ equal the definition's values for
 // ANY reference m, provided no exponent overflows; the row max is simply the
-// safe choice.  Here m is set to the exact running max on a wave's first tile
-// and on every masked tile (α = 2^(m_old − m_new) rescales ℓ and Oᵀ there, as
-// in safe_softmax_block); on the other tiles the old m is kept and the tile
-// is accepted if its per-lane sum of P stays below 2^20 — every P, and hence
-// ℓ and Oᵀ, is then far from overflow.  A tile that fails the check is redone
-// with the exact max update.  The common case thus costs no max reduction and
-// no rescale.  ℓ sums the fp32 P (summing the bf16-rounded P would move LSE by
+// safe choice.  The kernel first runs a fast pass: m is the exact running max
+// after a wave's first tile and after every masked tile (α = 2^(m_old − m_new)
+// rescales ℓ and Oᵀ there, as in safe_softmax_block), and is left unchanged
+// on the other tiles, which then need neither a max reduction nor a rescale.
+// P ≤ 2^(score − m) can only overflow if a later score exceeds the first
+// tile's max by about 2^7 in log2 units; the epilogue checks ℓ and Oᵀ, and if
+// any row of the workgroup is not finite the whole workgroup recomputes its
+// rows with the exact running-max update on every 32-key block (which cannot
+// overflow).  ℓ sums the fp32 P (summing the bf16-rounded P would move LSE by
 // up to 2^-9 on short rows).
 //
 // Register layouts.  The MFMA computes Sᵀ (keys × queries) so that a lane owns
@@ -33,15 +35,12 @@
 // registers 8c .. 8c + 7 of a block are directly the B operand of Oᵀ = Vᵀ·Pᵀ
 // for the 16 keys 16c + {4h .. 4h + 3, 8 + 4h .. 8 + 4h + 3}; Vᵀ is stored in
 // LDS with exactly those 8 keys in one 16-byte chunk, so the A operand is one
-// ds_read_b128.  K rows are padded (d = 128) or XOR-swizzled (d = 64) and the
-// Vᵀ chunks XOR-swizzled so that the MFMA operand reads are bank-conflict
-// free.
+// ds_read_b128.  K rows are padded and the Vᵀ chunks XOR-swizzled so that the
+// MFMA operand reads are bank-conflict free.
 #include "attn_common.h"
 
 namespace attn {
 namespace {
-
-constexpr float kSumLimit = 1048576.0f;  // 2^20: per-lane sum of P accepted without a new max
 
 template <int D>
 struct Cfg;
@@ -65,11 +64,11 @@ struct Cfg<128> {
 template <>
 struct Cfg<64> {
     static constexpr int BC = 128;
-    static constexpr int KROW = 64 * 2;  // XOR-swizzled K row
+    static constexpr int KROW = 64 * 2 + 16;  // padded K row
     static constexpr int VROW = BC * 2;
     static constexpr int K_BYTES = BC * KROW;
     static constexpr int V_BYTES = 64 * VROW;
-    __device__ static int kpos(int row, int ch) { return row * KROW + ((ch ^ ((row >> 1) & 7)) << 4); }
+    __device__ static int kpos(int row, int ch) { return row * KROW + ch * 16; }
     __device__ static int vpos(int d, int P) {
         const int x = d & 31;
         return d * VROW + ((P ^ ((x ^ (x >> 2)) & 15)) << 4);
@@ -99,7 +98,7 @@ struct Offsets {
     uint32_t k_st;                     // LDS, first K chunk of this thread
     uint32_t v_ld;                     // global, first V key of this thread (tile-relative)
     uint32_t v_st[4];                  // LDS, Vᵀ rows d0 .. d0+3 (relative to the V tile)
-    uint32_t k_rd[G::DCH];             // LDS, Sᵀ A operand, key block 0
+    uint32_t k_rd;                     // LDS, Sᵀ A operand, key block 0, d chunk 0
     uint32_t v_rd[G::KBLK][2];         // LDS, Oᵀ A operand, d block 0 (relative to the V tile)
 
     __device__ inline void init(int tid, int hl, int ql) {
@@ -112,8 +111,7 @@ struct Offsets {
         v_ld = (uint32_t)(key0 * D * 2 + d4 * 8);
 #pragma unroll
         for (int j = 0; j < 4; ++j) v_st[j] = (uint32_t)L::vpos(4 * d4 + j, P);
-#pragma unroll
-        for (int c = 0; c < G::DCH; ++c) k_rd[c] = (uint32_t)L::kpos(ql, 2 * c + hl);
+        k_rd = (uint32_t)L::kpos(ql, hl);  // chunk 2c + hl is 32c bytes further
 #pragma unroll
         for (int blk = 0; blk < G::KBLK; ++blk)
 #pragma unroll
@@ -220,33 +218,82 @@ __device__ inline void apply_mask(f32x16 (&s)[Geo<D>::KBLK], int kv0, int kv_len
         }
 }
 
-// One 32-key block of the online softmax: P (bf16 pairs) and the ℓ / Oᵀ / m
-// update.  `exact` (wave-uniform) asks for the running-max update of
-// safe_softmax_block; otherwise the reference max is kept unless the overflow
-// check fails, in which case the block is redone exactly.
+// Exact running-max update for one 32-key block (safe_softmax_block): new
+// max, α rescale of ℓ and Oᵀ, P as bf16 pairs.
 template <int D>
-__device__ inline void softmax_block(const f32x16& s, uint32_t (&pb)[8], WaveState<D>& w, float c2, bool exact) {
-    float m_new = w.m_run, m_use = w.m_run, lsum;
-    for (;;) {
-        if (exact) {
-            float mx = kNegInf;
+__device__ inline void softmax_block_exact(const f32x16& s, uint32_t (&pb)[8], WaveState<D>& w, float c2) {
+    float mx = kNegInf;
 #pragma unroll
-            for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[r], s[r + 1]));
-            m_new = fmaxf(w.m_run, pair_max(mx) * c2);
-            m_use = (m_new == kNegInf) ? 0.f : m_new;
+    for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[r], s[r + 1]));
+    const float m_new = fmaxf(w.m_run, pair_max(mx) * c2);
+    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+    const float lsum = exponentiate(s, pb, c2, m_use);
+    const float alpha = exp2_fast(w.m_run - m_use);
+    w.m_run = m_new;
+    w.l_run = w.l_run * alpha + lsum;
+#pragma unroll
+    for (int i = 0; i < Geo<D>::DBLK; ++i) w.acc[i] *= alpha;
+}
+
+template <int D>
+__device__ inline void pv_block(WaveState<D>& w, const char* vs, const Offsets<D>& o, int blk,
+                                const uint32_t (&pb)[8]) {
+#pragma unroll
+    for (int db = 0; db < Geo<D>::DBLK; ++db)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const uint4 a = *reinterpret_cast<const uint4*>(vs + o.v_rd[blk][c] + db * 32 * Cfg<D>::VROW);
+            const uint4 b = make_uint4(pb[4 * c], pb[4 * c + 1], pb[4 * c + 2], pb[4 * c + 3]);
+            w.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                                __builtin_bit_cast(bf16x8, b), w.acc[db], 0, 0, 0);
         }
-        lsum = exponentiate(s, pb, c2, m_use);
-        if (exact || __builtin_amdgcn_ballot_w64(lsum > kSumLimit) == 0) break;
-        exact = true;
-    }
-    if (exact) {
-        const float alpha = exp2_fast(w.m_run - m_use);
-        w.m_run = m_new;
-        w.l_run = w.l_run * alpha + lsum;
+}
+
+template <int D>
+__device__ inline void qk_tile(f32x16 (&s)[Geo<D>::KBLK], const char* ks, const Offsets<D>& o,
+                               const bf16x8 (&qf)[Geo<D>::DCH]) {
 #pragma unroll
-        for (int i = 0; i < Geo<D>::DBLK; ++i) w.acc[i] *= alpha;
-    } else {
-        w.l_run += lsum;
+    for (int blk = 0; blk < Geo<D>::KBLK; ++blk) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[blk][r] = 0.f;
+#pragma unroll
+        for (int c = 0; c < Geo<D>::DCH; ++c) {
+            const uint4 a = *reinterpret_cast<const uint4*>(ks + o.k_rd + blk * 32 * Cfg<D>::KROW + c * 32);
+            s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[c], s[blk], 0, 0, 0);
+        }
+    }
+}
+
+// Fast tile: unmasked, reference max kept (no reduction, no rescale).
+template <int D>
+__device__ inline void tile_fast(WaveState<D>& w, const char* stage, const Offsets<D>& o,
+                                 const bf16x8 (&qf)[Geo<D>::DCH], float c2) {
+    f32x16 s[Geo<D>::KBLK];
+    qk_tile<D>(s, stage, o, qf);
+    const float m_use = w.m_run;
+    const char* vs = stage + Cfg<D>::K_BYTES;
+#pragma unroll
+    for (int blk = 0; blk < Geo<D>::KBLK; ++blk) {
+        uint32_t pb[8];
+        w.l_run += exponentiate(s[blk], pb, c2, m_use);
+        pv_block<D>(w, vs, o, blk, pb);
+    }
+}
+
+// Exact tile: optional mask, running-max update on every 32-key block.
+template <int D, bool CAUSAL>
+__device__ inline void tile_exact(WaveState<D>& w, const char* stage, const Offsets<D>& o,
+                                  const bf16x8 (&qf)[Geo<D>::DCH], float c2, bool masked, int kv0,
+                                  int kv_len, int qrow, int hl) {
+    f32x16 s[Geo<D>::KBLK];
+    qk_tile<D>(s, stage, o, qf);
+    if (masked) apply_mask<D, CAUSAL>(s, kv0, kv_len, qrow, hl);
+    const char* vs = stage + Cfg<D>::K_BYTES;
+#pragma unroll
+    for (int blk = 0; blk < Geo<D>::KBLK; ++blk) {
+        uint32_t pb[8];
+        softmax_block_exact<D>(s[blk], pb, w, c2);
+        pv_block<D>(w, vs, o, blk, pb);
     }
 }
 
@@ -297,66 +344,52 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(Params p) {
     o.init(tid, hl, ql);
 
     WaveState<D> w;
-#pragma unroll
-    for (int i = 0; i < G::DBLK; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) w.acc[i][r] = 0.f;
-    w.m_run = kNegInf;
-    w.l_run = 0.f;
-    bool have_ref = false;  // wave-uniform: a reference max has been set
     const float c2 = p.scale_log2;
+    // First a fast pass; if any row of the workgroup overflowed, an exact pass.
+    for (bool exact_all = false;; exact_all = true) {
+#pragma unroll
+        for (int i = 0; i < G::DBLK; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) w.acc[i][r] = 0.f;
+        w.m_run = kNegInf;
+        w.l_run = 0.f;
 
-    KVRegs<D> pre;
-    if (ntiles > 0) load_kv<D>(pre, o, kres, vres, 0);
-
-    auto step = [&](auto stage_tag, int it) {
-        constexpr int ST = decltype(stage_tag)::value;
-        char* stage = smem + ST * G::STAGE;
-        store_kv<D>(pre, o, stage);
-        __syncthreads();
-        const int kv0 = it * BC;
-        if (it + 1 < ntiles) load_kv<D>(pre, o, kres, vres, kv0 + BC);
-        // Under a causal mask a wave whose rows all precede the tile skips it.
-        if (CAUSAL && kv0 > q0w + 31) return;
-
-        // ---- Sᵀ = K · Qᵀ
-        f32x16 s[G::KBLK];
-#pragma unroll
-        for (int blk = 0; blk < G::KBLK; ++blk) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) s[blk][r] = 0.f;
-#pragma unroll
-            for (int c = 0; c < G::DCH; ++c) {
-                const uint4 a = *reinterpret_cast<const uint4*>(stage + o.k_rd[c] + blk * 32 * L::KROW);
-                s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[c],
-                                                                 s[blk], 0, 0, 0);
-            }
-        }
-
-        // ---- online softmax and Oᵀ += Vᵀ · Pᵀ, one 32-key block at a time
-        const bool masked = (kv0 + BC > kv_len) || (CAUSAL && kv0 + BC - 1 > q0w);
-        if (masked) apply_mask<D, CAUSAL>(s, kv0, kv_len, qrow, hl);
-        const char* vs = stage + L::K_BYTES;
-#pragma unroll
-        for (int blk = 0; blk < G::KBLK; ++blk) {
-            uint32_t pb[8];
-            softmax_block<D>(s[blk], pb, w, c2, masked || !have_ref);
-            have_ref = true;
-#pragma unroll
-            for (int db = 0; db < G::DBLK; ++db)
-#pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    const uint4 a = *reinterpret_cast<const uint4*>(vs + o.v_rd[blk][c] + db * 32 * L::VROW);
-                    const uint4 b = make_uint4(pb[4 * c], pb[4 * c + 1], pb[4 * c + 2], pb[4 * c + 3]);
-                    w.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), w.acc[db], 0, 0, 0);
+        KVRegs<D> pre;
+        if (ntiles > 0) load_kv<D>(pre, o, kres, vres, 0);
+        // One pass over tiles [it0, it1): stage the tile in LDS, prefetch the
+        // next one, compute.  FAST: every tile is unmasked for every wave.
+        auto run = [&](auto fast_tag, int it0, int it1) {
+            constexpr bool FAST = decltype(fast_tag)::value;
+            for (int it = it0; it < it1; ++it) {
+                char* stage = smem + (it & 1) * G::STAGE;
+                store_kv<D>(pre, o, stage);
+                __syncthreads();
+                const int kv0 = it * BC;
+                if (it + 1 < ntiles) load_kv<D>(pre, o, kres, vres, kv0 + BC);
+                if (FAST) {
+                    tile_fast<D>(w, stage, o, qf, c2);
+                } else {
+                    // Under a causal mask a wave whose rows all precede the tile skips it.
+                    if (CAUSAL && kv0 > q0w + 31) continue;
+                    const bool masked = (kv0 + BC > kv_len) || (CAUSAL && kv0 + BC - 1 > q0w);
+                    tile_exact<D, CAUSAL>(w, stage, o, qf, c2, masked, kv0, kv_len, qrow, hl);
                 }
-        }
-    };
-
-    for (int it = 0; it < ntiles; it += 2) {
-        step(std::integral_constant<int, 0>{}, it);
-        if (it + 1 < ntiles) step(std::integral_constant<int, 1>{}, it + 1);
+            }
+        };
+        // Tiles before n_full are unmasked for every wave of the workgroup.
+        const int n_full = min(ntiles, (CAUSAL ? min(q0, kv_len) : kv_len) / BC);
+        const int n_fast_end = exact_all ? 1 : n_full;
+        run(std::false_type{}, 0, min(1, ntiles));
+        run(std::true_type{}, 1, n_fast_end);
+        run(std::false_type{}, max(1, n_fast_end), ntiles);
+        if (exact_all) break;
+        // overflow check: ℓ and every Oᵀ entry finite (inf · 0 and NaN · 0 are NaN)
+        float z = w.l_run * 0.f;
+#pragma unroll
+        for (int i = 0; i < G::DBLK; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) z = __builtin_fmaf(w.acc[i][r], 0.f, z);
+        if (!__syncthreads_or(!(z == 0.f))) break;
     }
 
     // ---- epilogue: O = Oᵀ/ℓ -> bf16, LSE

@@ -166,6 +166,27 @@ def test_one_hot_dominant_key(dev):
     assert float((lse - 60.0).abs().max()) <= 1e-3
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_late_dominant_key(dev, causal, d):
+    """A key far past the first tiles scores 150 above the rest (about 216 in
+    base-2 units, beyond the fp32 exponent range relative to the first tiles'
+    max).  O must be that key's V row and LSE its score; rows before it (under
+    the causal mask) must match the oracle."""
+    B, H, Hkv, N = 1, 2, 1, 700
+    _, k, v, _ = make_qkv(B, H, Hkv, N, d, "bf16", seed=18)
+    q = torch.zeros((B, H, N, d), dtype=torch.bfloat16)
+    q[..., 0] = 1.0
+    k[..., 0] = 0.0
+    k[0, 0, 600, 0] = 150.0
+    o, lse = run_gpu(dev, q, k, v, 1.0, causal, None)
+    O, L = oracle_of(q, k, v, 1.0, causal, None)
+    check(o, lse, O, L, TOL_O["bf16"], f"late dominant key d={d} causal={causal}")
+    rows = slice(600, N)
+    assert torch.equal(o[0, :, rows], v[0, 0, 600].expand(H, N - 600, d))
+    assert float((lse[0, :, rows] - 150.0).abs().max()) <= 1e-3
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_negative_scale(dev, dtype):
     B, H, Hkv, N, d = 1, 2, 1, 190, 128
