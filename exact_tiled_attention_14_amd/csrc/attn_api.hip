@@ -8,7 +8,7 @@
 #include "attn_common.h"
 
 namespace attn {
-hipError_t launch_fwd_bf16(const Params& p, int d, bool causal, hipStream_t stream);
+hipError_t launch_fwd_bf16(const Params& p, int d, bool causal, int ksplit, hipStream_t stream);
 hipError_t launch_fwd_f32(const Params& p, int d, bool causal, hipStream_t stream);
 }  // namespace attn
 
@@ -54,6 +54,26 @@ int validate(const void* q, const void* k, const void* v, const void* o, const v
     return ATTN_OK;
 }
 
+// Number of compute units of the current device (cached per device).
+int device_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+// Split each workgroup's key range over two wave groups when the grid alone
+// gives fewer than two workgroups per compute unit.
+int key_split(const attn::Params& p) {
+    const int64_t wgs = (int64_t)p.B * p.H * p.q_tiles;
+    return wgs < 2 * (int64_t)device_cus() ? 2 : 1;
+}
+
 }  // namespace
 
 extern "C" {
@@ -66,7 +86,7 @@ int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* l
     const int st = validate(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, key_lens, &p, &empty);
     if (st != ATTN_OK || empty) return st;
     (void)hipGetLastError();
-    const hipError_t e = attn::launch_fwd_bf16(p, d, causal != 0, static_cast<hipStream_t>(stream));
+    const hipError_t e = attn::launch_fwd_bf16(p, d, causal != 0, key_split(p), static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

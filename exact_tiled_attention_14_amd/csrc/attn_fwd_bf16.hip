@@ -297,15 +297,22 @@ __device__ inline void tile_exact(WaveState<D>& w, const char* stage, const Offs
     }
 }
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(Params p) {
+// KSPLIT = 2 runs two groups of four waves on the same 128 query rows: group
+// g takes the key tiles it ≡ g (mod 2), and at the end group 1 hands its
+// (Oᵀ, m, ℓ) to group 0 through LDS, where the two partial results over
+// disjoint key sets are combined by the softmax-merge rule (unite.ai page,
+// section "闪电注意力的数学原理", formula 2): m = max(m0, m1), each side scaled
+// by 2^(m_g − m).  It doubles the waves per SIMD when the grid alone cannot.
+template <int D, bool CAUSAL, int KSPLIT>
+__global__ __launch_bounds__(kThreads * KSPLIT, 2 / KSPLIT) void attn_fwd_bf16_kernel(Params p) {
     using G = Geo<D>;
-    using L = Cfg<D>;
     constexpr int BC = G::BC;
-    __shared__ __attribute__((aligned(16))) char smem[2 * G::STAGE];
+    __shared__ __attribute__((aligned(16))) char smem[2 * KSPLIT * G::STAGE];
 
-    const int tid = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tid = threadIdx.x % kThreads;  // thread index within the group
+    const int wave_all = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int grp = wave_all / kWaves;       // key-split group
+    const int wave = wave_all % kWaves;      // wave within the group
     const int lane = tid & 63;
     const int hl = lane >> 5, ql = lane & 31;
 
@@ -318,6 +325,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(Params p) {
     int kv_len;
     const int kv_hi = key_limit<CAUSAL>(p, t.b, q0, &kv_len);
     const int ntiles = (kv_hi + BC - 1) / BC;
+    const int niters = (ntiles + KSPLIT - 1) / KSPLIT;  // tile it = KSPLIT·j + grp
 
     const uint16_t* qp = static_cast<const uint16_t*>(p.q) + ((size_t)(t.b * p.H + t.h) * p.N) * D;
     const uint16_t* kb = static_cast<const uint16_t*>(p.k) + ((size_t)(t.b * p.Hkv + g) * p.N) * D;
@@ -342,6 +350,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(Params p) {
 
     Offsets<D> o;
     o.init(tid, hl, ql);
+    char* my_stages = smem + grp * 2 * G::STAGE;
 
     WaveState<D> w;
     const float c2 = p.scale_log2;
@@ -355,20 +364,22 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(Params p) {
         w.l_run = 0.f;
 
         KVRegs<D> pre;
-        if (ntiles > 0) load_kv<D>(pre, o, kres, vres, 0);
-        // One pass over tiles [it0, it1): stage the tile in LDS, prefetch the
+        if (grp < ntiles) load_kv<D>(pre, o, kres, vres, grp * BC);
+        // Iterations [j0, j1): stage this group's tile in LDS, prefetch its
         // next one, compute.  FAST: every tile is unmasked for every wave.
-        auto run = [&](auto fast_tag, int it0, int it1) {
+        auto run = [&](auto fast_tag, int j0, int j1) {
             constexpr bool FAST = decltype(fast_tag)::value;
-            for (int it = it0; it < it1; ++it) {
-                char* stage = smem + (it & 1) * G::STAGE;
-                store_kv<D>(pre, o, stage);
+            for (int j = j0; j < j1; ++j) {
+                const int it = KSPLIT * j + grp;
+                char* stage = my_stages + (j & 1) * G::STAGE;
+                if (it < ntiles) store_kv<D>(pre, o, stage);
                 __syncthreads();
                 const int kv0 = it * BC;
-                if (it + 1 < ntiles) load_kv<D>(pre, o, kres, vres, kv0 + BC);
+                if (it + KSPLIT < ntiles) load_kv<D>(pre, o, kres, vres, kv0 + KSPLIT * BC);
                 if (FAST) {
                     tile_fast<D>(w, stage, o, qf, c2);
                 } else {
+                    if (it >= ntiles) continue;
                     // Under a causal mask a wave whose rows all precede the tile skips it.
                     if (CAUSAL && kv0 > q0w + 31) continue;
                     const bool masked = (kv0 + BC > kv_len) || (CAUSAL && kv0 + BC - 1 > q0w);
@@ -376,12 +387,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(Params p) {
                 }
             }
         };
-        // Tiles before n_full are unmasked for every wave of the workgroup.
+        // Tiles before n_full are unmasked for every wave of the workgroup;
+        // iterations before j_full only touch such tiles in every group.
         const int n_full = min(ntiles, (CAUSAL ? min(q0, kv_len) : kv_len) / BC);
-        const int n_fast_end = exact_all ? 1 : n_full;
-        run(std::false_type{}, 0, min(1, ntiles));
-        run(std::true_type{}, 1, n_fast_end);
-        run(std::false_type{}, max(1, n_fast_end), ntiles);
+        const int j_full = exact_all ? 1 : n_full / KSPLIT;
+        run(std::false_type{}, 0, min(1, niters));
+        run(std::true_type{}, 1, j_full);
+        run(std::false_type{}, max(1, j_full), niters);
         if (exact_all) break;
         // overflow check: ℓ and every Oᵀ entry finite (inf · 0 and NaN · 0 are NaN)
         float z = w.l_run * 0.f;
@@ -390,6 +402,33 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(Params p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) z = __builtin_fmaf(w.acc[i][r], 0.f, z);
         if (!__syncthreads_or(!(z == 0.f))) break;
+    }
+
+    if (KSPLIT == 2) {
+        // merge group 1's partial result into group 0 (lane-contiguous LDS rows)
+        constexpr int NV = G::DBLK * 16 + 2;
+        float* xch = reinterpret_cast<float*>(smem) + (wave * NV) * 64 + lane;
+        __syncthreads();  // every group is done with its LDS stages
+        if (grp == 1) {
+#pragma unroll
+            for (int i = 0; i < G::DBLK; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) xch[(i * 16 + r) * 64] = w.acc[i][r];
+            xch[(NV - 2) * 64] = w.m_run;
+            xch[(NV - 1) * 64] = w.l_run;
+        }
+        __syncthreads();
+        if (grp == 1) return;
+        const float m1 = xch[(NV - 2) * 64], l1 = xch[(NV - 1) * 64];
+        const float m = fmaxf(w.m_run, m1);
+        const float m_use = (m == kNegInf) ? 0.f : m;
+        const float a0 = exp2_fast(w.m_run - m_use), a1 = exp2_fast(m1 - m_use);
+#pragma unroll
+        for (int i = 0; i < G::DBLK; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) w.acc[i][r] = a0 * w.acc[i][r] + a1 * xch[(i * 16 + r) * 64];
+        w.l_run = a0 * w.l_run + a1 * l1;
+        w.m_run = m;
     }
 
     // ---- epilogue: O = Oᵀ/ℓ -> bf16, LSE
@@ -413,16 +452,24 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(Params p) {
     }
 }
 
+template <int D, bool CAUSAL>
+void launch_d(const Params& p, int ksplit, hipStream_t stream) {
+    const dim3 grid((unsigned)(p.B * p.H * p.q_tiles));
+    if (ksplit == 2)
+        hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, 2>), grid, dim3(2 * kThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, 1>), grid, dim3(kThreads), 0, stream, p);
+}
+
 }  // namespace
 
-hipError_t launch_fwd_bf16(const Params& p, int d, bool causal, hipStream_t stream) {
-    const dim3 grid((unsigned)(p.B * p.H * p.q_tiles)), block(kThreads);
+hipError_t launch_fwd_bf16(const Params& p, int d, bool causal, int ksplit, hipStream_t stream) {
     if (d == 64) {
-        if (causal) hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, true>), grid, block, 0, stream, p);
-        else hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, false>), grid, block, 0, stream, p);
+        if (causal) launch_d<64, true>(p, ksplit, stream);
+        else launch_d<64, false>(p, ksplit, stream);
     } else {
-        if (causal) hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, true>), grid, block, 0, stream, p);
-        else hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, false>), grid, block, 0, stream, p);
+        if (causal) launch_d<128, true>(p, ksplit, stream);
+        else launch_d<128, false>(p, ksplit, stream);
     }
     return hipGetLastError();
 }

@@ -58,6 +58,9 @@ def oracle_of(q, k, v, scale, causal, key_lens, rows=None):
 SMALL = [  # (B, H, Hkv, N, d): several tiles, ragged tails, grouped heads
     (1, 1, 1, 1, 64), (2, 2, 1, 17, 64), (1, 4, 2, 100, 128), (2, 2, 2, 129, 64),
     (1, 2, 1, 255, 128), (1, 3, 3, 300, 64), (2, 4, 1, 520, 128),
+    # enough (b, h, query tile) work items that each workgroup keeps its whole
+    # key range (small grids split the key range over two wave groups)
+    (4, 64, 16, 260, 64), (2, 128, 32, 300, 128),
 ]
 
 
