@@ -47,7 +47,7 @@ struct Tile {
 };
 
 template <bool CAUSAL>
-__device__ inline Tile map_workgroup(const Params& p) {
+__device__ __forceinline__ Tile map_workgroup(const Params& p) {
     const int G = gridDim.x;
     const int w = blockIdx.x;
     const int x = w % kXcds, k = w / kXcds;
@@ -67,7 +67,7 @@ __device__ inline Tile map_workgroup(const Params& p) {
 // sequence (padded positions are ignored), cut under a causal mask at the
 // last query row of the tile.
 template <bool CAUSAL>
-__device__ inline int key_limit(const Params& p, int b, int q0, int* kv_len_out) {
+__device__ __forceinline__ int key_limit(const Params& p, int b, int q0, int* kv_len_out) {
     int kv_len = p.N;
     if (p.key_lens != nullptr) {
         const int kl = p.key_lens[b];
@@ -79,7 +79,7 @@ __device__ inline int key_limit(const Params& p, int b, int q0, int* kv_len_out)
     return lim;
 }
 
-__device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Raw buffer loads: a descriptor covers `bytes` bytes from `base`; a load
 // whose bytes lie beyond that range returns zeros instead of touching memory.
@@ -88,21 +88,21 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kBufferDword3 = 0x00020000;  // gfx9 raw-buffer format word
 
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferDword3);
 }
-__device__ inline uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
     return make_uint4(v.x, v.y, v.z, v.w);
 }
-__device__ inline uint2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+__device__ __forceinline__ uint2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
     return make_uint2(v.x, v.y);
 }
 
 // Value of lane (lane ^ 32): the other half-wave, which holds the same query
 // rows for the other half of the keys.
-__device__ inline float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
+__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLn2 = 0.693147180559945309f;

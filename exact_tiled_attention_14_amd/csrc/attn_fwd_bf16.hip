@@ -53,9 +53,9 @@ struct Cfg<128> {
     static constexpr int K_BYTES = BC * KROW;
     static constexpr int V_BYTES = 128 * VROW;
     // byte offset of 16-byte chunk `ch` of K row `row` in the K tile
-    __device__ static int kpos(int row, int ch) { return row * KROW + ch * 16; }
+    __device__ __forceinline__ static int kpos(int row, int ch) { return row * KROW + ch * 16; }
     // byte offset of key-chunk P of Vᵀ row d in the Vᵀ tile
-    __device__ static int vpos(int d, int P) {
+    __device__ __forceinline__ static int vpos(int d, int P) {
         const int x = d & 31;
         return d * VROW + ((P ^ ((x ^ (x >> 3)) & 7)) << 4);
     }
@@ -68,8 +68,8 @@ struct Cfg<64> {
     static constexpr int VROW = BC * 2;
     static constexpr int K_BYTES = BC * KROW;
     static constexpr int V_BYTES = 64 * VROW;
-    __device__ static int kpos(int row, int ch) { return row * KROW + ch * 16; }
-    __device__ static int vpos(int d, int P) {
+    __device__ __forceinline__ static int kpos(int row, int ch) { return row * KROW + ch * 16; }
+    __device__ __forceinline__ static int vpos(int d, int P) {
         const int x = d & 31;
         return d * VROW + ((P ^ ((x ^ (x >> 2)) & 15)) << 4);
     }
@@ -101,7 +101,7 @@ struct Offsets {
     uint32_t k_rd;                     // LDS, Sᵀ A operand, key block 0, d chunk 0
     uint32_t v_rd[G::KBLK][2];         // LDS, Oᵀ A operand, d block 0 (relative to the V tile)
 
-    __device__ inline void init(int tid, int hl, int ql) {
+    __device__ __forceinline__ void init(int tid, int hl, int ql) {
         const int row = tid / G::CPR, ch = tid % G::CPR;
         k_ld = (uint32_t)(row * D * 2 + ch * 16);
         k_st = (uint32_t)L::kpos(row, ch);  // the swizzle ignores row bits >= 4
@@ -130,7 +130,7 @@ struct KVRegs {
 // loads past it return zeros: NaN or any other content there can never reach
 // the output (0 · NaN would otherwise be NaN).
 template <int D>
-__device__ inline void load_kv(KVRegs<D>& r, const Offsets<D>& o, __amdgpu_buffer_rsrc_t kres,
+__device__ __forceinline__ void load_kv(KVRegs<D>& r, const Offsets<D>& o, __amdgpu_buffer_rsrc_t kres,
                                __amdgpu_buffer_rsrc_t vres, int kv0) {
     const uint32_t base = (uint32_t)kv0 * (D * 2);
 #pragma unroll
@@ -142,7 +142,7 @@ __device__ inline void load_kv(KVRegs<D>& r, const Offsets<D>& o, __amdgpu_buffe
 
 // Registers -> LDS stage: K rows, and V transposed into key chunks.
 template <int D>
-__device__ inline void store_kv(const KVRegs<D>& r, const Offsets<D>& o, char* stage) {
+__device__ __forceinline__ void store_kv(const KVRegs<D>& r, const Offsets<D>& o, char* stage) {
     char* vs = stage + Cfg<D>::K_BYTES;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -166,18 +166,18 @@ __device__ inline void store_kv(const KVRegs<D>& r, const Offsets<D>& o, char* s
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-__device__ inline uint32_t pack_bf16x2(float lo, float hi) {
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     const f32x2 v = {lo, hi};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // max / sum of x over the lane pair (lane, lane ^ 32): v_permlane32_swap hands
 // each lane its partner's value in one of the two results, itself in the other.
-__device__ inline float pair_max(float x) {
+__device__ __forceinline__ float pair_max(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-__device__ inline float pair_sum(float x) {
+__device__ __forceinline__ float pair_sum(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
@@ -191,7 +191,7 @@ struct WaveState {
 
 // P = 2^(S·c − m) of one 32-key block into bf16 pairs; returns this lane's
 // sum of the fp32 P.  Masked scores are −∞ and c > 0, so they give P = 0.
-__device__ inline float exponentiate(const f32x16& s, uint32_t (&pb)[8], float c2, float m_use) {
+__device__ __forceinline__ float exponentiate(const f32x16& s, uint32_t (&pb)[8], float c2, float m_use) {
     float l0 = 0.f, l1 = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
@@ -204,24 +204,22 @@ __device__ inline float exponentiate(const f32x16& s, uint32_t (&pb)[8], float c
     return l0 + l1;
 }
 
-// Inadmissible keys of a tile (past the valid key length, or after the query
-// row under a causal mask) get score −∞.
-template <int D, bool CAUSAL>
-__device__ inline void apply_mask(f32x16 (&s)[Geo<D>::KBLK], int kv0, int kv_len, int qrow, int hl) {
+// Inadmissible keys of 32-key block `blk` (past the valid key length, or
+// after the query row under a causal mask) get score −∞.
+template <bool CAUSAL>
+__device__ __forceinline__ void apply_mask(f32x16& s, int blk, int kv0, int kv_len, int qrow, int hl) {
 #pragma unroll
-    for (int blk = 0; blk < Geo<D>::KBLK; ++blk)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int key = kv0 + blk * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-            const bool ok = key < kv_len && (!CAUSAL || key <= qrow);
-            s[blk][r] = ok ? s[blk][r] : kNegInf;
-        }
+    for (int r = 0; r < 16; ++r) {
+        const int key = kv0 + blk * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+        const bool ok = key < kv_len && (!CAUSAL || key <= qrow);
+        s[r] = ok ? s[r] : kNegInf;
+    }
 }
 
 // Exact running-max update for one 32-key block (safe_softmax_block): new
 // max, α rescale of ℓ and Oᵀ, P as bf16 pairs.
 template <int D>
-__device__ inline void softmax_block_exact(const f32x16& s, uint32_t (&pb)[8], WaveState<D>& w, float c2) {
+__device__ __forceinline__ void softmax_block_exact(const f32x16& s, uint32_t (&pb)[8], WaveState<D>& w, float c2) {
     float mx = kNegInf;
 #pragma unroll
     for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[r], s[r + 1]));
@@ -236,7 +234,7 @@ __device__ inline void softmax_block_exact(const f32x16& s, uint32_t (&pb)[8], W
 }
 
 template <int D>
-__device__ inline void pv_block(WaveState<D>& w, const char* vs, const Offsets<D>& o, int blk,
+__device__ __forceinline__ void pv_block(WaveState<D>& w, const char* vs, const Offsets<D>& o, int blk,
                                 const uint32_t (&pb)[8]) {
 #pragma unroll
     for (int db = 0; db < Geo<D>::DBLK; ++db)
@@ -250,50 +248,50 @@ __device__ inline void pv_block(WaveState<D>& w, const char* vs, const Offsets<D
 }
 
 template <int D>
-__device__ inline void qk_tile(f32x16 (&s)[Geo<D>::KBLK], const char* ks, const Offsets<D>& o,
-                               const bf16x8 (&qf)[Geo<D>::DCH]) {
+__device__ __forceinline__ void qk_block(f32x16& s, const char* ks, const Offsets<D>& o,
+                                         const bf16x8 (&qf)[Geo<D>::DCH], int blk) {
 #pragma unroll
-    for (int blk = 0; blk < Geo<D>::KBLK; ++blk) {
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[blk][r] = 0.f;
+    for (int c = 0; c < Geo<D>::DCH; ++c) {
+        const uint4 a = *reinterpret_cast<const uint4*>(ks + o.k_rd + blk * 32 * Cfg<D>::KROW + c * 32);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[c], s, 0, 0, 0);
+    }
+}
+
+// One tile, one 32-key block at a time: the next block's Sᵀ is issued before
+// this block's exponentials so that MFMA and VALU work interleave, with at
+// most two Sᵀ blocks live.  MODE 0: the wave's first tile — block 0's row max
+// becomes the reference m (Oᵀ and ℓ are still zero); MODE 1: unmasked tile,
+// reference kept; MODE 2: exact running-max update on every block.
+template <int D, bool CAUSAL, int MODE>
+__device__ __forceinline__ void tile(WaveState<D>& w, const char* stage, const Offsets<D>& o,
+                                     const bf16x8 (&qf)[Geo<D>::DCH], float c2, bool masked, int kv0,
+                                     int kv_len, int qrow, int hl) {
+    constexpr int KBLK = Geo<D>::KBLK;
+    f32x16 s[2];
+    qk_block<D>(s[0], stage, o, qf, 0);
+    const char* vs = stage + Cfg<D>::K_BYTES;
 #pragma unroll
-        for (int c = 0; c < Geo<D>::DCH; ++c) {
-            const uint4 a = *reinterpret_cast<const uint4*>(ks + o.k_rd + blk * 32 * Cfg<D>::KROW + c * 32);
-            s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[c], s[blk], 0, 0, 0);
+    for (int blk = 0; blk < KBLK; ++blk) {
+        if (blk + 1 < KBLK) qk_block<D>(s[(blk + 1) & 1], stage, o, qf, blk + 1);
+        f32x16& sb = s[blk & 1];
+        if (MODE != 1 && masked) apply_mask<CAUSAL>(sb, blk, kv0, kv_len, qrow, hl);
+        uint32_t pb[8];
+        if (MODE == 2) {
+            softmax_block_exact<D>(sb, pb, w, c2);
+        } else {
+            if (MODE == 0 && blk == 0) {
+                float mx = kNegInf;
+#pragma unroll
+                for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sb[r], sb[r + 1]));
+                w.m_run = pair_max(mx) * c2;
+            }
+            const float m_use = (w.m_run == kNegInf) ? 0.f : w.m_run;
+            w.l_run += exponentiate(sb, pb, c2, m_use);
         }
-    }
-}
-
-// Fast tile: unmasked, reference max kept (no reduction, no rescale).
-template <int D>
-__device__ inline void tile_fast(WaveState<D>& w, const char* stage, const Offsets<D>& o,
-                                 const bf16x8 (&qf)[Geo<D>::DCH], float c2) {
-    f32x16 s[Geo<D>::KBLK];
-    qk_tile<D>(s, stage, o, qf);
-    const float m_use = w.m_run;
-    const char* vs = stage + Cfg<D>::K_BYTES;
-#pragma unroll
-    for (int blk = 0; blk < Geo<D>::KBLK; ++blk) {
-        uint32_t pb[8];
-        w.l_run += exponentiate(s[blk], pb, c2, m_use);
         pv_block<D>(w, vs, o, blk, pb);
-    }
-}
-
-// Exact tile: optional mask, running-max update on every 32-key block.
-template <int D, bool CAUSAL>
-__device__ inline void tile_exact(WaveState<D>& w, const char* stage, const Offsets<D>& o,
-                                  const bf16x8 (&qf)[Geo<D>::DCH], float c2, bool masked, int kv0,
-                                  int kv_len, int qrow, int hl) {
-    f32x16 s[Geo<D>::KBLK];
-    qk_tile<D>(s, stage, o, qf);
-    if (masked) apply_mask<D, CAUSAL>(s, kv0, kv_len, qrow, hl);
-    const char* vs = stage + Cfg<D>::K_BYTES;
-#pragma unroll
-    for (int blk = 0; blk < Geo<D>::KBLK; ++blk) {
-        uint32_t pb[8];
-        softmax_block_exact<D>(s[blk], pb, w, c2);
-        pv_block<D>(w, vs, o, blk, pb);
+        if (MODE == 1) __builtin_amdgcn_sched_barrier(0);  // keep the block pipeline order
     }
 }
 
@@ -366,9 +364,11 @@ __global__ __launch_bounds__(kThreads * KSPLIT, 2 / KSPLIT) void attn_fwd_bf16_k
         KVRegs<D> pre;
         if (grp < ntiles) load_kv<D>(pre, o, kres, vres, grp * BC);
         // Iterations [j0, j1): stage this group's tile in LDS, prefetch its
-        // next one, compute.  FAST: every tile is unmasked for every wave.
-        auto run = [&](auto fast_tag, int j0, int j1) {
-            constexpr bool FAST = decltype(fast_tag)::value;
+        // next one, compute.  MODE 0: the group's first tile; 1 (fast): every
+        // tile is unmasked for every wave; 2: exact running-max update.
+        auto run = [&](auto mode_tag, int j0, int j1) __attribute__((always_inline)) {
+            constexpr int MODE = decltype(mode_tag)::value;
+            constexpr bool FAST = MODE == 1;
             for (int j = j0; j < j1; ++j) {
                 const int it = KSPLIT * j + grp;
                 char* stage = my_stages + (j & 1) * G::STAGE;
@@ -377,23 +377,27 @@ __global__ __launch_bounds__(kThreads * KSPLIT, 2 / KSPLIT) void attn_fwd_bf16_k
                 const int kv0 = it * BC;
                 if (it + KSPLIT < ntiles) load_kv<D>(pre, o, kres, vres, kv0 + KSPLIT * BC);
                 if (FAST) {
-                    tile_fast<D>(w, stage, o, qf, c2);
+                    tile<D, CAUSAL, 1>(w, stage, o, qf, c2, false, kv0, kv_len, qrow, hl);
                 } else {
                     if (it >= ntiles) continue;
                     // Under a causal mask a wave whose rows all precede the tile skips it.
                     if (CAUSAL && kv0 > q0w + 31) continue;
                     const bool masked = (kv0 + BC > kv_len) || (CAUSAL && kv0 + BC - 1 > q0w);
-                    tile_exact<D, CAUSAL>(w, stage, o, qf, c2, masked, kv0, kv_len, qrow, hl);
+                    tile<D, CAUSAL, MODE>(w, stage, o, qf, c2, masked, kv0, kv_len, qrow, hl);
                 }
             }
         };
         // Tiles before n_full are unmasked for every wave of the workgroup;
         // iterations before j_full only touch such tiles in every group.
         const int n_full = min(ntiles, (CAUSAL ? min(q0, kv_len) : kv_len) / BC);
-        const int j_full = exact_all ? 1 : n_full / KSPLIT;
-        run(std::false_type{}, 0, min(1, niters));
-        run(std::true_type{}, 1, j_full);
-        run(std::false_type{}, max(1, j_full), niters);
+        if (exact_all) {
+            run(std::integral_constant<int, 2>{}, 0, niters);
+        } else {
+            const int j_full = n_full / KSPLIT;
+            run(std::integral_constant<int, 0>{}, 0, min(1, niters));
+            run(std::integral_constant<int, 1>{}, 1, j_full);
+            run(std::integral_constant<int, 2>{}, max(1, j_full), niters);
+        }
         if (exact_all) break;
         // overflow check: ℓ and every Oᵀ entry finite (inf · 0 and NaN · 0 are NaN)
         float z = w.l_run * 0.f;
