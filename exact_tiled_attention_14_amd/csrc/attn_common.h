@@ -37,8 +37,11 @@ struct Params {
 
 // Workgroup -> (b, h, query tile).  The hardware deals consecutive workgroup
 // ids round-robin over the 8 XCDs (each with its own L2), so logical ids are
-// renumbered to give every XCD one contiguous run of (b, h, tile) work: the
-// query tiles of a head, which all stream that head's K/V, then share one L2.
+// renumbered to give every XCD one contiguous run of (h, b, tile) work: the
+// query tiles of a head, which all stream that head's K/V, then share one L2,
+// and consecutive heads (one KV group under GQA) sit together.  The batch is
+// the inner index so that sequences of different key lengths are spread over
+// all XCDs instead of loading some XCDs with only the longest ones.
 // Under a causal mask tiles are issued longest first (load balance, one of the
 // FlashAttention-2 improvements listed in the FlashAttention2 code block of
 // the zsdodo.com page).
@@ -53,12 +56,12 @@ __device__ __forceinline__ Tile map_workgroup(const Params& p) {
     const int x = w % kXcds, k = w / kXcds;
     const int per = G / kXcds, extra = G % kXcds;
     const int logical = x * per + min(x, extra) + k;
-    const int bh = logical / p.q_tiles;
-    int t = logical - bh * p.q_tiles;
+    const int hb = logical / p.q_tiles;
+    int t = logical - hb * p.q_tiles;
     if (CAUSAL) t = p.q_tiles - 1 - t;
     Tile r;
-    r.b = bh / p.H;
-    r.h = bh - r.b * p.H;
+    r.h = hb / p.B;
+    r.b = hb - r.h * p.B;
     r.tile = t;
     return r;
 }
