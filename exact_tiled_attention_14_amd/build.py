@@ -10,6 +10,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libattn.so")
+INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 SOURCES = ["attn_api.hip", "attn_fwd_bf16.hip", "attn_fwd_f32.hip"]
 
 # Packed fp32 VALU forms are disabled: the code below is written for plain
@@ -31,7 +32,7 @@ def build(verbose=False):
 
     def compile_one(src):
         obj = os.path.join(out, src + ".o")
-        cmd = [_hipcc(), *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [_hipcc(), *HIP_FLAGS, "-I" + INCLUDE, "-c", os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")

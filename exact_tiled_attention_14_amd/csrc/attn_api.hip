@@ -4,11 +4,11 @@
 #include <math.h>
 #include <stdint.h>
 
-#include "../../include/attn.h"
+#include "attn.h"
 #include "attn_common.h"
 
 namespace attn {
-hipError_t launch_fwd_bf16(const Params& p, int d, bool causal, int ksplit, hipStream_t stream);
+hipError_t launch_fwd_bf16(const Params& p, int d, bool causal, const Schedule& sc, hipStream_t stream);
 hipError_t launch_fwd_f32(const Params& p, int d, bool causal, hipStream_t stream);
 }  // namespace attn
 
@@ -67,11 +67,27 @@ int device_cus() {
     return cached[dev];
 }
 
-// Split each workgroup's key range over two wave groups when the grid alone
-// gives fewer than two workgroups per compute unit.
-int key_split(const attn::Params& p) {
-    const int64_t wgs = (int64_t)p.B * p.H * p.q_tiles;
-    return wgs < 2 * (int64_t)device_cus() ? 2 : 1;
+// Launch shape of the bf16 kernel.  Under a causal mask query tiles differ
+// in cost (tile + 1 key tiles); when there are few of them per CU (fewer than
+// four) the hardware's in-order dispatch cannot balance them, so persistent
+// workgroups, one per CU with two wave groups each, are dealt a balanced
+// (zig-zag, longest first) list.  Otherwise one workgroup per query tile,
+// issued longest first; the key range is split over two wave groups when the
+// grid has fewer than two workgroups per CU.
+attn::Schedule schedule_bf16(const attn::Params& p, bool causal) {
+    const int64_t items = (int64_t)p.B * p.H * p.q_tiles;
+    const int cus = device_cus();
+    attn::Schedule sc;
+    if (causal && items < 4 * (int64_t)cus) {
+        sc.ksplit = 2;
+        sc.persistent = 1;
+        sc.grid = (int)(items < cus ? items : cus);
+    } else {
+        sc.ksplit = items < 2 * (int64_t)cus ? 2 : 1;
+        sc.persistent = 0;
+        sc.grid = (int)items;
+    }
+    return sc;
 }
 
 }  // namespace
@@ -86,7 +102,8 @@ int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* l
     const int st = validate(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, key_lens, &p, &empty);
     if (st != ATTN_OK || empty) return st;
     (void)hipGetLastError();
-    const hipError_t e = attn::launch_fwd_bf16(p, d, causal != 0, key_split(p), static_cast<hipStream_t>(stream));
+    const hipError_t e =
+        attn::launch_fwd_bf16(p, d, causal != 0, schedule_bf16(p, causal != 0), static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

@@ -35,6 +35,14 @@ struct Params {
                         // every score is 0, computed as q = 0 with c = 1
 };
 
+// Launch shape chosen on the host: key-range split (1 or 2 wave groups),
+// persistent causal schedule, number of workgroups.
+struct Schedule {
+    int ksplit;
+    int persistent;
+    int grid;
+};
+
 // Workgroup -> (b, h, query tile).  The hardware deals consecutive workgroup
 // ids round-robin over the 8 XCDs (each with its own L2), so logical ids are
 // renumbered to give every XCD one contiguous run of (h, b, tile) work: the

@@ -302,10 +302,9 @@ __device__ __forceinline__ void tile(WaveState<D>& w, const char* stage, const O
 // section "闪电注意力的数学原理", formula 2): m = max(m0, m1), each side scaled
 // by 2^(m_g − m).  It doubles the waves per SIMD when the grid alone cannot.
 template <int D, bool CAUSAL, int KSPLIT>
-__global__ __launch_bounds__(kThreads * KSPLIT, 2 / KSPLIT) void attn_fwd_bf16_kernel(Params p) {
+__device__ __forceinline__ void attend_tile(const Params& p, const Tile& t, char* smem) {
     using G = Geo<D>;
     constexpr int BC = G::BC;
-    __shared__ __attribute__((aligned(16))) char smem[2 * KSPLIT * G::STAGE];
 
     const int tid = threadIdx.x % kThreads;  // thread index within the group
     const int wave_all = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
@@ -314,7 +313,6 @@ __global__ __launch_bounds__(kThreads * KSPLIT, 2 / KSPLIT) void attn_fwd_bf16_k
     const int lane = tid & 63;
     const int hl = lane >> 5, ql = lane & 31;
 
-    const Tile t = map_workgroup<CAUSAL>(p);
     const int q0 = t.tile * kBR;
     const int q0w = q0 + wave * 32;
     const int qrow = q0w + ql;
@@ -422,7 +420,7 @@ __global__ __launch_bounds__(kThreads * KSPLIT, 2 / KSPLIT) void attn_fwd_bf16_k
             xch[(NV - 1) * 64] = w.l_run;
         }
         __syncthreads();
-        if (grp == 1) return;
+        if (grp == 1) return;  // group 0 writes the rows
         const float m1 = xch[(NV - 2) * 64], l1 = xch[(NV - 1) * 64];
         const float m = fmaxf(w.m_run, m1);
         const float m_use = (m == kNegInf) ? 0.f : m;
@@ -456,24 +454,79 @@ __global__ __launch_bounds__(kThreads * KSPLIT, 2 / KSPLIT) void attn_fwd_bf16_k
     }
 }
 
+
+// Persistent schedule for causal masks: work items (b, h, query tile) cost
+// about tile + 1 key tiles.  Each XCD owns a contiguous range of heads (its
+// L2 then holds their K/V); inside the range the items are ranked longest
+// first and dealt to the XCD's workgroups in zig-zag order (k, 2n−1−k, 2n+k,
+// …), so every workgroup — and with one workgroup per CU every CU — gets
+// about the same total work.  Returns false when workgroup `blockIdx.x` has
+// no item of round `i`.
+__device__ __forceinline__ bool persistent_item(const Params& p, int i, Tile* t) {
+    const int G = gridDim.x, w = blockIdx.x;
+    const int heads = p.B * p.H;  // head index hb = h·B + b
+    const int T = p.q_tiles;
+    int h0, nh, nwg, k;
+    if (heads >= kXcds && G >= kXcds) {
+        const int x = w % kXcds;
+        k = w / kXcds;
+        nwg = G / kXcds + (x < G % kXcds ? 1 : 0);
+        h0 = (int)((int64_t)heads * x / kXcds);
+        nh = (int)((int64_t)heads * (x + 1) / kXcds) - h0;
+    } else {
+        h0 = 0;
+        nh = heads;
+        nwg = G;
+        k = w;
+    }
+    const int64_t r = (i & 1) ? (int64_t)(i + 1) * nwg - 1 - k : (int64_t)i * nwg + k;
+    if (r >= (int64_t)nh * T) return false;
+    const int hb = h0 + (int)(r % nh);
+    t->tile = T - 1 - (int)(r / nh);
+    t->h = hb / p.B;
+    t->b = hb - t->h * p.B;
+    return true;
+}
+
+template <int D, bool CAUSAL, int KSPLIT, bool PERSIST>
+__global__ __launch_bounds__(kThreads * KSPLIT, 2 / KSPLIT) void attn_fwd_bf16_kernel(Params p) {
+    __shared__ __attribute__((aligned(16))) char smem[2 * KSPLIT * Geo<D>::STAGE];
+    if (!PERSIST) {
+        attend_tile<D, CAUSAL, KSPLIT>(p, map_workgroup<CAUSAL>(p), smem);
+        return;
+    }
+    Tile t;
+    for (int i = 0; persistent_item(p, i, &t); ++i) {
+        if (i > 0) __syncthreads();  // the previous item's LDS traffic is done
+        attend_tile<D, CAUSAL, KSPLIT>(p, t, smem);
+    }
+}
+
 template <int D, bool CAUSAL>
-void launch_d(const Params& p, int ksplit, hipStream_t stream) {
-    const dim3 grid((unsigned)(p.B * p.H * p.q_tiles));
-    if (ksplit == 2)
-        hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, 2>), grid, dim3(2 * kThreads), 0, stream, p);
-    else
-        hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, 1>), grid, dim3(kThreads), 0, stream, p);
+void launch_d(const Params& p, const Schedule& sc, hipStream_t stream) {
+    const dim3 grid((unsigned)sc.grid);
+    if (sc.ksplit == 2) {
+        if (sc.persistent)
+            hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, 2, true>), grid, dim3(2 * kThreads), 0, stream, p);
+        else
+            hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, 2, false>), grid, dim3(2 * kThreads), 0, stream, p);
+    } else {
+        if (sc.persistent)
+            hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, 1, true>), grid, dim3(kThreads), 0, stream, p);
+        else
+            hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, 1, false>), grid, dim3(kThreads), 0, stream, p);
+    }
 }
 
 }  // namespace
 
-hipError_t launch_fwd_bf16(const Params& p, int d, bool causal, int ksplit, hipStream_t stream) {
+hipError_t launch_fwd_bf16(const Params& p, int d, bool causal, const Schedule& sc, hipStream_t stream) {
     if (d == 64) {
-        if (causal) launch_d<64, true>(p, ksplit, stream);
-        else launch_d<64, false>(p, ksplit, stream);
+        if (causal) launch_d<64, true>(p, sc, stream);
+        else launch_d<64, false>(p, sc, stream);
     } else {
-        if (causal) launch_d<128, true>(p, ksplit, stream);
-        else launch_d<128, false>(p, ksplit, stream);
+        if (causal) launch_d<128, true>(p, sc, stream);
+        else launch_d<128, false>(p, sc, stream);
     }
     return hipGetLastError();
 }

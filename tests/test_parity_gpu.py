@@ -61,6 +61,8 @@ SMALL = [  # (B, H, Hkv, N, d): several tiles, ragged tails, grouped heads
     # enough (b, h, query tile) work items that each workgroup keeps its whole
     # key range (small grids split the key range over two wave groups)
     (4, 64, 16, 260, 64), (2, 128, 32, 300, 128),
+    # enough causal query tiles per CU for the non-persistent causal schedule
+    (8, 64, 16, 300, 64),
 ]
 
 
