@@ -259,27 +259,32 @@ __device__ __forceinline__ void qk_block(f32x16& s, const char* ks, const Offset
     }
 }
 
-// One tile, one 32-key block at a time: the next block's Sᵀ is issued before
-// this block's exponentials so that MFMA and VALU work interleave, with at
-// most two Sᵀ blocks live.  MODE 0: the wave's first tile — block 0's row max
-// becomes the reference m (Oᵀ and ℓ are still zero); MODE 1: unmasked tile,
-// reference kept; MODE 2: exact running-max update on every block.
+// One tile, one 32-key block at a time, software-pipelined so that each
+// step has matrix work independent of its vector work: step b issues the Sᵀ
+// MFMAs of block b + 1 and the Oᵀ MFMAs of block b − 1 (whose P is ready)
+// while it exponentiates block b; the last block's Oᵀ MFMAs close the tile.
+// At most two Sᵀ and two P blocks are live.  MODE 0: the wave's first tile —
+// block 0's row max becomes the reference m (Oᵀ and ℓ are still zero);
+// MODE 1: unmasked tile, reference kept; MODE 2: exact running-max update on
+// every block (its α rescale of Oᵀ follows the previous block's Oᵀ MFMAs and
+// precedes this block's).
 template <int D, bool CAUSAL, int MODE>
 __device__ __forceinline__ void tile(WaveState<D>& w, const char* stage, const Offsets<D>& o,
                                      const bf16x8 (&qf)[Geo<D>::DCH], float c2, bool masked, int kv0,
                                      int kv_len, int qrow, int hl) {
     constexpr int KBLK = Geo<D>::KBLK;
     f32x16 s[2];
+    uint32_t pb[2][8];
     qk_block<D>(s[0], stage, o, qf, 0);
     const char* vs = stage + Cfg<D>::K_BYTES;
 #pragma unroll
     for (int blk = 0; blk < KBLK; ++blk) {
         if (blk + 1 < KBLK) qk_block<D>(s[(blk + 1) & 1], stage, o, qf, blk + 1);
+        if (blk > 0) pv_block<D>(w, vs, o, blk - 1, pb[(blk - 1) & 1]);
         f32x16& sb = s[blk & 1];
         if (MODE != 1 && masked) apply_mask<CAUSAL>(sb, blk, kv0, kv_len, qrow, hl);
-        uint32_t pb[8];
         if (MODE == 2) {
-            softmax_block_exact<D>(sb, pb, w, c2);
+            softmax_block_exact<D>(sb, pb[blk & 1], w, c2);
         } else {
             if (MODE == 0 && blk == 0) {
                 float mx = kNegInf;
@@ -288,11 +293,11 @@ __device__ __forceinline__ void tile(WaveState<D>& w, const char* stage, const O
                 w.m_run = pair_max(mx) * c2;
             }
             const float m_use = (w.m_run == kNegInf) ? 0.f : w.m_run;
-            w.l_run += exponentiate(sb, pb, c2, m_use);
+            w.l_run += exponentiate(sb, pb[blk & 1], c2, m_use);
         }
-        pv_block<D>(w, vs, o, blk, pb);
         if (MODE == 1) __builtin_amdgcn_sched_barrier(0);  // keep the block pipeline order
     }
+    pv_block<D>(w, vs, o, KBLK - 1, pb[(KBLK - 1) & 1]);
 }
 
 // KSPLIT = 2 runs two groups of four waves on the same 128 query rows: group
@@ -330,19 +335,16 @@ __device__ __forceinline__ void attend_tile(const Params& p, const Tile& t, char
     const __amdgpu_buffer_rsrc_t vres = make_rsrc(vb, (uint32_t)kv_len * (D * 2));
 
     // Q rows of this lane as the Sᵀ B operand: chunk c holds d = 16c + 8h .. +7.
-    bf16x8 qf[G::DCH];
+    // The sign flip / zeroing is applied after the first K/V tile's loads
+    // are issued, so that nothing waits on the Q loads before those start.
+    uint4 qu[G::DCH];
     {
         const __amdgpu_buffer_rsrc_t qres = make_rsrc(qp, (uint32_t)p.N * (D * 2));
-        const uint32_t flip = p.negate_q ? 0x80008000u : 0u;
-        const uint32_t keep = p.zero_q ? 0u : 0xffffffffu;
 #pragma unroll
-        for (int c = 0; c < G::DCH; ++c) {
-            uint4 u = buf_load16(qres, (uint32_t)qrow * (D * 2) + c * 32 + hl * 16);
-            u.x = (u.x ^ flip) & keep; u.y = (u.y ^ flip) & keep;
-            u.z = (u.z ^ flip) & keep; u.w = (u.w ^ flip) & keep;
-            qf[c] = __builtin_bit_cast(bf16x8, u);
-        }
+        for (int c = 0; c < G::DCH; ++c) qu[c] = buf_load16(qres, (uint32_t)qrow * (D * 2) + c * 32 + hl * 16);
     }
+    uint32_t flip = p.negate_q ? 0x80008000u : 0u;
+    uint32_t keep = p.zero_q ? 0u : 0xffffffffu;
 
     Offsets<D> o;
     o.init(tid, hl, ql);
@@ -361,6 +363,16 @@ __device__ __forceinline__ void attend_tile(const Params& p, const Tile& t, char
 
         KVRegs<D> pre;
         if (grp < ntiles) load_kv<D>(pre, o, kres, vres, grp * BC);
+        // (identity on the exact pass: flip and keep are reset below)
+        bf16x8 qf[G::DCH];
+#pragma unroll
+        for (int c = 0; c < G::DCH; ++c) {
+            qu[c].x = (qu[c].x ^ flip) & keep; qu[c].y = (qu[c].y ^ flip) & keep;
+            qu[c].z = (qu[c].z ^ flip) & keep; qu[c].w = (qu[c].w ^ flip) & keep;
+            qf[c] = __builtin_bit_cast(bf16x8, qu[c]);
+        }
+        flip = 0u;
+        keep = 0xffffffffu;
         // Iterations [j0, j1): stage this group's tile in LDS, prefetch its
         // next one, compute.  MODE 0: the group's first tile; 1 (fast): every
         // tile is unmasked for every wave; 2: exact running-max update.
