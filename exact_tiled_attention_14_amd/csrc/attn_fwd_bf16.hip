@@ -17,15 +17,16 @@
 //
 // Reference value m.  O/ℓ and m + log2 ℓ equal the definition's values for
 // ANY reference m, provided no exponent overflows; the row max is simply the
-// safe choice.  The kernel first runs a fast pass: m is the exact running max
-// after a wave's first tile and after every masked tile (α = 2^(m_old − m_new)
-// rescales ℓ and Oᵀ there, as in safe_softmax_block), and is left unchanged
-// on the other tiles, which then need neither a max reduction nor a rescale.
-// P ≤ 2^(score − m) can only overflow if a later score exceeds the first
-// tile's max by about 2^7 in log2 units; the epilogue checks ℓ and Oᵀ, and if
-// any row of the workgroup is not finite the whole workgroup recomputes its
-// rows with the exact running-max update on every 32-key block (which cannot
-// overflow).  ℓ sums the fp32 P (summing the bf16-rounded P would move LSE by
+// safe choice.  The kernel first runs a fast pass: m is the max of the first
+// 32-key block of the wave's first tile and is left unchanged on every later
+// tile, masked or not, which then needs neither a max reduction nor a
+// rescale.  m never exceeds the row max, so the row max's P is at least 1
+// (ℓ cannot underflow to 0); P ≤ 2^(score − m) can only overflow if a later
+// score exceeds that first block's max by about 2^7 in log2 units.  The
+// epilogue checks ℓ and Oᵀ, and if any row of the workgroup is not finite the
+// whole workgroup recomputes its rows with the exact running-max update
+// (safe_softmax_block: α = 2^(m_old − m_new) rescales ℓ and Oᵀ) on every
+// 32-key block, which cannot overflow.  ℓ sums the fp32 P (summing the bf16-rounded P would move LSE by
 // up to 2^-9 on short rows).
 //
 // Register layouts.  The MFMA computes Sᵀ (keys × queries) so that a lane owns
@@ -265,9 +266,10 @@ __device__ __forceinline__ void qk_block(f32x16& s, const char* ks, const Offset
 // while it exponentiates block b; the last block's Oᵀ MFMAs close the tile.
 // At most two Sᵀ and two P blocks are live.  MODE 0: the wave's first tile —
 // block 0's row max becomes the reference m (Oᵀ and ℓ are still zero);
-// MODE 1: unmasked tile, reference kept; MODE 2: exact running-max update on
-// every block (its α rescale of Oᵀ follows the previous block's Oᵀ MFMAs and
-// precedes this block's).
+// MODE 1: unmasked tile, reference kept; MODE 3: reference kept, mask applied
+// when `masked`; MODE 2: exact running-max update on every block (its α
+// rescale of Oᵀ follows the previous block's Oᵀ MFMAs and precedes this
+// block's).
 template <int D, bool CAUSAL, int MODE>
 __device__ __forceinline__ void tile(WaveState<D>& w, const char* stage, const Offsets<D>& o,
                                      const bf16x8 (&qf)[Geo<D>::DCH], float c2, bool masked, int kv0,
@@ -375,7 +377,8 @@ __device__ __forceinline__ void attend_tile(const Params& p, const Tile& t, char
         keep = 0xffffffffu;
         // Iterations [j0, j1): stage this group's tile in LDS, prefetch its
         // next one, compute.  MODE 0: the group's first tile; 1 (fast): every
-        // tile is unmasked for every wave; 2: exact running-max update.
+        // tile is unmasked for every wave; 3: reference kept, tiles masked
+        // where needed; 2: exact running-max update (the retry pass).
         auto run = [&](auto mode_tag, int j0, int j1) __attribute__((always_inline)) {
             constexpr int MODE = decltype(mode_tag)::value;
             constexpr bool FAST = MODE == 1;
@@ -406,7 +409,7 @@ __device__ __forceinline__ void attend_tile(const Params& p, const Tile& t, char
             const int j_full = n_full / KSPLIT;
             run(std::integral_constant<int, 0>{}, 0, min(1, niters));
             run(std::integral_constant<int, 1>{}, 1, j_full);
-            run(std::integral_constant<int, 2>{}, max(1, j_full), niters);
+            run(std::integral_constant<int, 3>{}, max(1, j_full), niters);
         }
         if (exact_all) break;
         // overflow check: ℓ and every Oᵀ entry finite (inf · 0 and NaN · 0 are NaN)
