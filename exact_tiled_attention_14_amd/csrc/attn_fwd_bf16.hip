@@ -30,14 +30,26 @@
 // up to 2^-9 on short rows).
 //
 // Register layouts.  The MFMA computes Sᵀ (keys × queries) so that a lane owns
-// ONE query row (lane % 32) and 16 keys of every 32-key block — MFMA output
-// row 8a + 4h + b (a < 4, b < 4) sits in register 4a + b of half-wave h — so
-// row sums are in-lane plus one exchange with lane ^ 32.  Rounded to bf16, the
-// registers 8c .. 8c + 7 of a block are directly the B operand of Oᵀ = Vᵀ·Pᵀ
-// for the 16 keys 16c + {4h .. 4h + 3, 8 + 4h .. 8 + 4h + 3}; Vᵀ is stored in
-// LDS with exactly those 8 keys in one 16-byte chunk, so the A operand is one
-// ds_read_b128.  K rows are padded and the Vᵀ chunks XOR-swizzled so that the
-// MFMA operand reads are bank-conflict free.
+// ONE query row (lane % 32) and 16 keys of every 32-key block, so row sums are
+// in-lane plus one exchange with lane ^ 32.  Lane L reads K row swap23(L % 32)
+// (bits 2 and 3 of the row index exchanged) as its A operand; MFMA output row
+// 8a + 4h + b sits in register 4a + b of half-wave h, so register r of half h
+// holds key 16(r / 8) + 8h + (r % 8).  Rounded to bf16, registers 8c .. 8c + 7
+// are then directly the B operand of Oᵀ = Vᵀ·Pᵀ for the 8 consecutive keys
+// 16c + 8h .. 16c + 8h + 7, and the matching A operand (those keys at one d)
+// comes from V stored row-major in LDS through two ds_read_b64_tr_b16 (the
+// transposing LDS read of gfx950: within each 16-lane group, lane i receives
+// element i % 4 of the 8-byte pieces addressed by lanes i / 4, 4 + i / 4,
+// 8 + i / 4 and 12 + i / 4).
+//
+// Data movement.  K and V tiles go from HBM straight to LDS with
+// buffer_load_dwordx4 … lds (16 bytes per lane, 1 KiB per wave instruction,
+// no registers); a load past the descriptor's end (the key length) writes
+// zeros.  K rows are padded to 2d + 16 bytes and V rows have their 64-byte
+// quarters (d = 128) or halves (d = 64) XOR-swizzled by the key index, so
+// both operand reads are bank-conflict free; the loads write those layouts
+// directly because each lane picks the global 16 bytes that belong at its LDS
+// position.
 #include "attn_common.h"
 
 namespace attn {
@@ -49,30 +61,28 @@ struct Cfg;
 template <>
 struct Cfg<128> {
     static constexpr int BC = 64;
-    static constexpr int KROW = 128 * 2 + 16;  // padded K row
-    static constexpr int VROW = BC * 2;
+    static constexpr int KROW = 128 * 2 + 16;  // padded K row (bytes)
+    static constexpr int VROW = 128 * 2;       // V row (bytes)
     static constexpr int K_BYTES = BC * KROW;
-    static constexpr int V_BYTES = 128 * VROW;
-    // byte offset of 16-byte chunk `ch` of K row `row` in the K tile
-    __device__ __forceinline__ static int kpos(int row, int ch) { return row * KROW + ch * 16; }
-    // byte offset of key-chunk P of Vᵀ row d in the Vᵀ tile
-    __device__ __forceinline__ static int vpos(int d, int P) {
-        const int x = d & 31;
-        return d * VROW + ((P ^ ((x ^ (x >> 3)) & 7)) << 4);
+    static constexpr int V_BYTES = BC * VROW;
+    // LDS byte offset, in the V tile, of byte x of V row `key`: the row's
+    // 64-byte quarters are XOR-swizzled by key % 4 (an involution: the same
+    // map sends an LDS position back to its row byte)
+    __device__ __forceinline__ static int vpos(int key, int x) {
+        return key * VROW + ((((x >> 6) ^ (key & 3)) << 6) | (x & 63));
     }
 };
 
 template <>
 struct Cfg<64> {
     static constexpr int BC = 128;
-    static constexpr int KROW = 64 * 2 + 16;  // padded K row
-    static constexpr int VROW = BC * 2;
+    static constexpr int KROW = 64 * 2 + 16;
+    static constexpr int VROW = 64 * 2;
     static constexpr int K_BYTES = BC * KROW;
-    static constexpr int V_BYTES = 64 * VROW;
-    __device__ __forceinline__ static int kpos(int row, int ch) { return row * KROW + ch * 16; }
-    __device__ __forceinline__ static int vpos(int d, int P) {
-        const int x = d & 31;
-        return d * VROW + ((P ^ ((x ^ (x >> 2)) & 15)) << 4);
+    static constexpr int V_BYTES = BC * VROW;
+    // 64-byte halves XOR-swizzled by bit 1 of the key
+    __device__ __forceinline__ static int vpos(int key, int x) {
+        return key * VROW + ((((x >> 6) ^ ((key >> 1) & 1)) << 6) | (x & 63));
     }
 };
 
@@ -83,86 +93,82 @@ struct Geo {
     static constexpr int KBLK = BC / 32;   // 32-key MFMA blocks per tile
     static constexpr int DCH = D / 16;     // 16-wide d chunks (Sᵀ k steps)
     static constexpr int DBLK = D / 32;    // 32-row blocks of Oᵀ
-    static constexpr int CPR = D / 8;      // 16-byte chunks per K row
     static constexpr int STAGE = L::K_BYTES + L::V_BYTES;
+    static constexpr int NK = L::K_BYTES / 1024;  // 1 KiB direct-load instructions per K tile
+    static constexpr int NV = L::V_BYTES / 1024;
+    static constexpr int KI = (NK + kWaves - 1) / kWaves;  // per wave
+    static constexpr int VI = NV / kWaves;
+    static_assert(L::K_BYTES % 1024 == 0 && NV % kWaves == 0, "tiles must split into 1 KiB wave loads");
 };
 
-// Per-thread byte offsets, fixed for the whole kernel.  Offsets that differ
-// between a thread's accesses only by a compile-time constant are kept once.
+__device__ __forceinline__ int swap23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+// Per-lane byte offsets, fixed for the whole kernel.
 template <int D>
 struct Offsets {
     using G = Geo<D>;
     using L = Cfg<D>;
-    // K chunk i of a thread: idx = tid + 256 i, i.e. row + i·(256/CPR), same column
-    static constexpr int KROWS_PER_PASS = kThreads / G::CPR;
-    uint32_t k_ld;                     // global, first K chunk of this thread (tile-relative)
-    uint32_t k_st;                     // LDS, first K chunk of this thread
-    uint32_t v_ld;                     // global, first V key of this thread (tile-relative)
-    uint32_t v_st[4];                  // LDS, Vᵀ rows d0 .. d0+3 (relative to the V tile)
-    uint32_t k_rd;                     // LDS, Sᵀ A operand, key block 0, d chunk 0
-    uint32_t v_rd[G::KBLK][2];         // LDS, Oᵀ A operand, d block 0 (relative to the V tile)
+    uint32_t k_src[G::KI];   // global offset (in the tile) of the 16 bytes this lane moves in K load i
+    uint32_t v_src[G::VI];
+    uint32_t k_rd;           // LDS: Sᵀ A operand, key block 0, d chunk 0
+    uint32_t v_rd[G::DBLK];  // LDS (in the V tile): Oᵀ A operand of d block db, key block 0, c = 0, keys + 0..3
 
-    __device__ __forceinline__ void init(int tid, int hl, int ql) {
-        const int row = tid / G::CPR, ch = tid % G::CPR;
-        k_ld = (uint32_t)(row * D * 2 + ch * 16);
-        k_st = (uint32_t)L::kpos(row, ch);  // the swizzle ignores row bits >= 4
-        // Vᵀ chunk P of this thread holds keys 16(P>>1) + 4(P&1) + {0..3, 8..11}
-        const int P = tid / (D / 4), d4 = tid % (D / 4);
-        const int key0 = 16 * (P >> 1) + 4 * (P & 1);
-        v_ld = (uint32_t)(key0 * D * 2 + d4 * 8);
+    __device__ __forceinline__ void init(int wave, int lane) {
+        const int hl = lane >> 5, ql = lane & 31;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) v_st[j] = (uint32_t)L::vpos(4 * d4 + j, P);
-        k_rd = (uint32_t)L::kpos(ql, hl);  // chunk 2c + hl is 32c bytes further
-#pragma unroll
-        for (int blk = 0; blk < G::KBLK; ++blk)
-#pragma unroll
-            for (int c = 0; c < 2; ++c) v_rd[blk][c] = (uint32_t)L::vpos(ql, blk * 4 + c * 2 + hl);
-    }
-};
-
-template <int D>
-struct KVRegs {
-    uint4 k[4];  // 4 x 16 bytes of K per thread (1024 chunks per tile)
-    uint2 v[8];  // 8 keys x 4 d of V per thread (for the transposed store)
-};
-
-// Global -> registers for the tile starting at key kv0.  The buffer
-// descriptors end at the last valid key (padding and the sequence end), so
-// loads past it return zeros: NaN or any other content there can never reach
-// the output (0 · NaN would otherwise be NaN).
-template <int D>
-__device__ __forceinline__ void load_kv(KVRegs<D>& r, const Offsets<D>& o, __amdgpu_buffer_rsrc_t kres,
-                               __amdgpu_buffer_rsrc_t vres, int kv0) {
-    const uint32_t base = (uint32_t)kv0 * (D * 2);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        r.k[i] = buf_load16(kres, base + o.k_ld + i * Offsets<D>::KROWS_PER_PASS * (D * 2));
-#pragma unroll
-    for (int s = 0; s < 8; ++s) r.v[s] = buf_load8(vres, base + o.v_ld + ((s & 3) + 8 * (s >> 2)) * (D * 2));
-}
-
-// Registers -> LDS stage: K rows, and V transposed into key chunks.
-template <int D>
-__device__ __forceinline__ void store_kv(const KVRegs<D>& r, const Offsets<D>& o, char* stage) {
-    char* vs = stage + Cfg<D>::K_BYTES;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<uint4*>(stage + o.k_st + i * Offsets<D>::KROWS_PER_PASS * Cfg<D>::KROW) = r.k[i];
-    // r.v[s] = {V[key s][d0], V[key s][d0+1]}, {V[key s][d0+2], V[key s][d0+3]};
-    // row d0 + j of Vᵀ gets the 8 keys' element j, two keys per dword.
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        uint32_t w[4];
-#pragma unroll
-        for (int pr = 0; pr < 4; ++pr) {
-            const uint32_t a = (j < 2) ? r.v[2 * pr].x : r.v[2 * pr].y;
-            const uint32_t b = (j < 2) ? r.v[2 * pr + 1].x : r.v[2 * pr + 1].y;
-            // low half from key 2pr, high half from key 2pr + 1
-            w[pr] = __builtin_amdgcn_perm(b, a, (j & 1) ? 0x07060302u : 0x05040100u);
+        for (int i = 0; i < G::KI; ++i) {
+            const int pos = 1024 * (wave + kWaves * i) + 16 * lane;  // LDS byte in the K tile
+            const int row = pos / L::KROW, off = pos % L::KROW;
+            // the 16 pad bytes of a row take a copy of the row's first chunk
+            k_src[i] = (uint32_t)(row * D * 2 + (off < D * 2 ? off : 0));
         }
-        *reinterpret_cast<uint4*>(vs + o.v_st[j]) = make_uint4(w[0], w[1], w[2], w[3]);
+#pragma unroll
+        for (int i = 0; i < G::VI; ++i) {
+            const int pos = 1024 * (wave + kWaves * i) + 16 * lane;  // LDS byte in the V tile
+            const int key = pos / L::VROW;
+            v_src[i] = (uint32_t)(key * D * 2 + (L::vpos(key, pos % L::VROW) - key * L::VROW));
+        }
+        k_rd = (uint32_t)(swap23(ql) * L::KROW + hl * 16);  // chunk 2c + hl is 32c bytes further
+        // ds_read_b64_tr_b16: lane 16g + k addresses key 8(g / 2) + k / 4 at
+        // d = 32 db + 16 (g % 2) + 4 (k % 4) .. + 3
+        const int g = lane >> 4, k = lane & 15;
+        const int key = 8 * (g >> 1) + (k >> 2);
+#pragma unroll
+        for (int db = 0; db < G::DBLK; ++db) v_rd[db] = (uint32_t)L::vpos(key, 2 * (32 * db + 16 * (g & 1) + 4 * (k & 3)));
     }
+};
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// One K/V tile (keys kv0 .. kv0 + BC − 1 of the head) straight into an LDS
+// stage: each wave issues its share of the 1 KiB loads.  The descriptors
+// start at key kv0 and end at the key length, so rows past it are zeros:
+// NaN or any other content there can never reach the output.
+template <int D>
+__device__ __forceinline__ void load_tile(const Offsets<D>& o, char* stage, const uint16_t* kb,
+                                          const uint16_t* vb, int kv0, int kv_len, int wave) {
+#if defined(__HIP_DEVICE_COMPILE__)  // (the LDS-destination builtin does not exist for the host pass)
+    using G = Geo<D>;
+    const uint32_t bytes = (uint32_t)(kv_len - kv0) * (D * 2);
+    const __amdgpu_buffer_rsrc_t kres = make_rsrc(kb + (size_t)kv0 * D, bytes);
+    const __amdgpu_buffer_rsrc_t vres = make_rsrc(vb + (size_t)kv0 * D, bytes);
+#pragma unroll
+    for (int i = 0; i < G::KI; ++i) {
+        const int t = wave + kWaves * i;
+        if (t < G::NK) __builtin_amdgcn_raw_ptr_buffer_load_lds(kres, (lds_void*)(stage + 1024 * t), 16, o.k_src[i], 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < G::VI; ++i) {
+        const int t = wave + kWaves * i;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vres, (lds_void*)(stage + Cfg<D>::K_BYTES + 1024 * t), 16, o.v_src[i], 0,
+                                                 0, 0);
+    }
+#endif
 }
+
+// This wave's direct loads have landed in LDS (the barrier that follows makes
+// every wave's visible).
+__device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); /* vmcnt(0) */ }
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -211,7 +217,7 @@ template <bool CAUSAL>
 __device__ __forceinline__ void apply_mask(f32x16& s, int blk, int kv0, int kv_len, int qrow, int hl) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-        const int key = kv0 + blk * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+        const int key = kv0 + blk * 32 + 16 * (r >> 3) + 8 * hl + (r & 7);
         const bool ok = key < kv_len && (!CAUSAL || key <= qrow);
         s[r] = ok ? s[r] : kNegInf;
     }
@@ -234,17 +240,23 @@ __device__ __forceinline__ void softmax_block_exact(const f32x16& s, uint32_t (&
     for (int i = 0; i < Geo<D>::DBLK; ++i) w.acc[i] *= alpha;
 }
 
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
 template <int D>
 __device__ __forceinline__ void pv_block(WaveState<D>& w, const char* vs, const Offsets<D>& o, int blk,
-                                const uint32_t (&pb)[8]) {
+                                         const uint32_t (&pb)[8]) {
+    constexpr int VROW = Cfg<D>::VROW;
 #pragma unroll
     for (int db = 0; db < Geo<D>::DBLK; ++db)
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            const uint4 a = *reinterpret_cast<const uint4*>(vs + o.v_rd[blk][c] + db * 32 * Cfg<D>::VROW);
+            const char* at = vs + o.v_rd[db] + (32 * blk + 16 * c) * VROW;
+            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)at);
+            const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(at + 4 * VROW));
+            const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
             const uint4 b = make_uint4(pb[4 * c], pb[4 * c + 1], pb[4 * c + 2], pb[4 * c + 3]);
-            w.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                                __builtin_bit_cast(bf16x8, b), w.acc[db], 0, 0, 0);
+            w.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, b), w.acc[db], 0, 0, 0);
         }
 }
 
@@ -302,6 +314,14 @@ __device__ __forceinline__ void tile(WaveState<D>& w, const char* stage, const O
     pv_block<D>(w, vs, o, KBLK - 1, pb[(KBLK - 1) & 1]);
 }
 
+// LDS stages: two separate __shared__ objects of KSPLIT stages each; group g
+// double-buffers in (s0 + g·STAGE, s1 + g·STAGE).
+template <int D, int KSPLIT>
+struct Lds {
+    char* s0;
+    char* s1;
+};
+
 // KSPLIT = 2 runs two groups of four waves on the same 128 query rows: group
 // g takes the key tiles it ≡ g (mod 2), and at the end group 1 hands its
 // (Oᵀ, m, ℓ) to group 0 through LDS, where the two partial results over
@@ -309,7 +329,7 @@ __device__ __forceinline__ void tile(WaveState<D>& w, const char* stage, const O
 // section "闪电注意力的数学原理", formula 2): m = max(m0, m1), each side scaled
 // by 2^(m_g − m).  It doubles the waves per SIMD when the grid alone cannot.
 template <int D, bool CAUSAL, int KSPLIT>
-__device__ __forceinline__ void attend_tile(const Params& p, const Tile& t, char* smem) {
+__device__ __forceinline__ void attend_tile(const Params& p, const Tile& t, const Lds<D, KSPLIT>& lds) {
     using G = Geo<D>;
     constexpr int BC = G::BC;
 
@@ -333,8 +353,6 @@ __device__ __forceinline__ void attend_tile(const Params& p, const Tile& t, char
     const uint16_t* qp = static_cast<const uint16_t*>(p.q) + ((size_t)(t.b * p.H + t.h) * p.N) * D;
     const uint16_t* kb = static_cast<const uint16_t*>(p.k) + ((size_t)(t.b * p.Hkv + g) * p.N) * D;
     const uint16_t* vb = static_cast<const uint16_t*>(p.v) + ((size_t)(t.b * p.Hkv + g) * p.N) * D;
-    const __amdgpu_buffer_rsrc_t kres = make_rsrc(kb, (uint32_t)kv_len * (D * 2));
-    const __amdgpu_buffer_rsrc_t vres = make_rsrc(vb, (uint32_t)kv_len * (D * 2));
 
     // Q rows of this lane as the Sᵀ B operand: chunk c holds d = 16c + 8h .. +7.
     // The sign flip / zeroing is applied after the first K/V tile's loads
@@ -349,8 +367,10 @@ __device__ __forceinline__ void attend_tile(const Params& p, const Tile& t, char
     uint32_t keep = p.zero_q ? 0u : 0xffffffffu;
 
     Offsets<D> o;
-    o.init(tid, hl, ql);
-    char* my_stages = smem + grp * 2 * G::STAGE;
+    o.init(wave, lane);
+    // this group's two stages (in distinct LDS objects; see Lds)
+    char* const S0 = lds.s0 + grp * G::STAGE;
+    char* const S1 = lds.s1 + grp * G::STAGE;
 
     WaveState<D> w;
     const float c2 = p.scale_log2;
@@ -363,8 +383,7 @@ __device__ __forceinline__ void attend_tile(const Params& p, const Tile& t, char
         w.m_run = kNegInf;
         w.l_run = 0.f;
 
-        KVRegs<D> pre;
-        if (grp < ntiles) load_kv<D>(pre, o, kres, vres, grp * BC);
+        if (grp < ntiles) load_tile<D>(o, S0, kb, vb, grp * BC, kv_len, wave);
         // (identity on the exact pass: flip and keep are reset below)
         bf16x8 qf[G::DCH];
 #pragma unroll
@@ -375,29 +394,40 @@ __device__ __forceinline__ void attend_tile(const Params& p, const Tile& t, char
         }
         flip = 0u;
         keep = 0xffffffffu;
-        // Iterations [j0, j1): stage this group's tile in LDS, prefetch its
-        // next one, compute.  MODE 0: the group's first tile; 1 (fast): every
-        // tile is unmasked for every wave; 3: reference kept, tiles masked
-        // where needed; 2: exact running-max update (the retry pass).
+        wait_loads();
+        __syncthreads();
+        // Iteration j computes on stage j & 1 while the group's next tile is
+        // loaded into the other stage; the barrier closing the iteration
+        // makes that stage visible and frees stage j & 1 for the load after.
+        // MODE 0: the group's first tile; 1 (fast): every tile is unmasked
+        // for every wave; 3: reference kept, tiles masked where needed;
+        // 2: exact running-max update (the retry pass).
         auto run = [&](auto mode_tag, int j0, int j1) __attribute__((always_inline)) {
             constexpr int MODE = decltype(mode_tag)::value;
             constexpr bool FAST = MODE == 1;
-            for (int j = j0; j < j1; ++j) {
+            // iteration j: compute on `cur` (stage j & 1), load into `next`
+            auto step = [&](int j, const char* cur, char* next) __attribute__((always_inline)) {
                 const int it = KSPLIT * j + grp;
-                char* stage = my_stages + (j & 1) * G::STAGE;
-                if (it < ntiles) store_kv<D>(pre, o, stage);
-                __syncthreads();
                 const int kv0 = it * BC;
-                if (it + KSPLIT < ntiles) load_kv<D>(pre, o, kres, vres, kv0 + KSPLIT * BC);
+                if (it + KSPLIT < ntiles) load_tile<D>(o, next, kb, vb, kv0 + KSPLIT * BC, kv_len, wave);
                 if (FAST) {
-                    tile<D, CAUSAL, 1>(w, stage, o, qf, c2, false, kv0, kv_len, qrow, hl);
-                } else {
-                    if (it >= ntiles) continue;
-                    // Under a causal mask a wave whose rows all precede the tile skips it.
-                    if (CAUSAL && kv0 > q0w + 31) continue;
+                    tile<D, CAUSAL, 1>(w, cur, o, qf, c2, false, kv0, kv_len, qrow, hl);
+                } else if (it < ntiles && !(CAUSAL && kv0 > q0w + 31)) {
+                    // (under a causal mask a wave whose rows all precede the tile skips it)
                     const bool masked = (kv0 + BC > kv_len) || (CAUSAL && kv0 + BC - 1 > q0w);
-                    tile<D, CAUSAL, MODE>(w, stage, o, qf, c2, masked, kv0, kv_len, qrow, hl);
+                    tile<D, CAUSAL, MODE>(w, cur, o, qf, c2, masked, kv0, kv_len, qrow, hl);
                 }
+                wait_loads();
+                __syncthreads();
+            };
+            // Unrolled by two so that every access names its stage object:
+            // the compiler can then tell the loads into one stage from the
+            // reads of the other and does not wait on the former for the latter.
+            int j = j0;
+            if ((j & 1) && j < j1) step(j++, S1, S0);
+            for (; j < j1; j += 2) {
+                step(j, S0, S1);
+                if (j + 1 < j1) step(j + 1, S1, S0);
             }
         };
         // Tiles before n_full are unmasked for every wave of the workgroup;
@@ -424,7 +454,8 @@ __device__ __forceinline__ void attend_tile(const Params& p, const Tile& t, char
     if (KSPLIT == 2) {
         // merge group 1's partial result into group 0 (lane-contiguous LDS rows)
         constexpr int NV = G::DBLK * 16 + 2;
-        float* xch = reinterpret_cast<float*>(smem) + (wave * NV) * 64 + lane;
+        static_assert(KSPLIT == 1 || kWaves * NV * 64 * 4 <= KSPLIT * G::STAGE, "the merge rows must fit in s0");
+        float* xch = reinterpret_cast<float*>(lds.s0) + (wave * NV) * 64 + lane;
         __syncthreads();  // every group is done with its LDS stages
         if (grp == 1) {
 #pragma unroll
@@ -505,15 +536,17 @@ __device__ __forceinline__ bool persistent_item(const Params& p, int i, Tile* t)
 
 template <int D, bool CAUSAL, int KSPLIT, bool PERSIST>
 __global__ __launch_bounds__(kThreads * KSPLIT, 2 / KSPLIT) void attn_fwd_bf16_kernel(Params p) {
-    __shared__ __attribute__((aligned(16))) char smem[2 * KSPLIT * Geo<D>::STAGE];
+    __shared__ __attribute__((aligned(16))) char s0[KSPLIT * Geo<D>::STAGE];
+    __shared__ __attribute__((aligned(16))) char s1[KSPLIT * Geo<D>::STAGE];
+    const Lds<D, KSPLIT> lds{s0, s1};
     if (!PERSIST) {
-        attend_tile<D, CAUSAL, KSPLIT>(p, map_workgroup<CAUSAL>(p), smem);
+        attend_tile<D, CAUSAL, KSPLIT>(p, map_workgroup<CAUSAL>(p), lds);
         return;
     }
     Tile t;
     for (int i = 0; persistent_item(p, i, &t); ++i) {
         if (i > 0) __syncthreads();  // the previous item's LDS traffic is done
-        attend_tile<D, CAUSAL, KSPLIT>(p, t, smem);
+        attend_tile<D, CAUSAL, KSPLIT>(p, t, lds);
     }
 }
 
