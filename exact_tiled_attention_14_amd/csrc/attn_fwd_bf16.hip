@@ -420,14 +420,21 @@ __device__ __forceinline__ void attend_tile(const Params& p, const Tile& t, cons
                 wait_loads();
                 __syncthreads();
             };
-            // Unrolled by two so that every access names its stage object:
-            // the compiler can then tell the loads into one stage from the
-            // reads of the other and does not wait on the former for the latter.
-            int j = j0;
-            if ((j & 1) && j < j1) step(j++, S1, S0);
-            for (; j < j1; j += 2) {
-                step(j, S0, S1);
-                if (j + 1 < j1) step(j + 1, S1, S0);
+            // The fast loop is unrolled by two so that every access names
+            // its stage object: the compiler can then tell the loads into one
+            // stage from the reads of the other and does not wait on the
+            // former for the latter.  The other modes (the first tile, masked
+            // tiles, the retry pass) are rare; they keep one copy of the code
+            // and accept that wait.
+            if constexpr (MODE == 1) {
+                int j = j0;
+                if ((j & 1) && j < j1) step(j++, S1, S0);
+                for (; j < j1; j += 2) {
+                    step(j, S0, S1);
+                    if (j + 1 < j1) step(j + 1, S1, S0);
+                }
+            } else {
+                for (int j = j0; j < j1; ++j) step(j, (j & 1) ? S1 : S0, (j & 1) ? S0 : S1);
             }
         };
         // Tiles before n_full are unmasked for every wave of the workgroup;
