@@ -276,16 +276,16 @@ __device__ __forceinline__ void qk_block(f32x16& s, const char* ks, const Offset
 // step has matrix work independent of its vector work: step b issues the Sᵀ
 // MFMAs of block b + 1 and the Oᵀ MFMAs of block b − 1 (whose P is ready)
 // while it exponentiates block b; the last block's Oᵀ MFMAs close the tile.
-// At most two Sᵀ and two P blocks are live.  MODE 0: the wave's first tile —
-// block 0's row max becomes the reference m (Oᵀ and ℓ are still zero);
-// MODE 1: unmasked tile, reference kept; MODE 3: reference kept, mask applied
-// when `masked`; MODE 2: exact running-max update on every block (its α
-// rescale of Oᵀ follows the previous block's Oᵀ MFMAs and precedes this
-// block's).
+// At most two Sᵀ and two P blocks are live.  MODE 1: unmasked tile,
+// reference m kept; MODE 3: reference kept, mask applied when `masked`, and
+// on the group's first tile (`first`) block 0's row max becomes the reference
+// (Oᵀ and ℓ are still zero there); MODE 2: exact running-max update on every
+// block (its α rescale of Oᵀ follows the previous block's Oᵀ MFMAs and
+// precedes this block's).
 template <int D, bool CAUSAL, int MODE>
 __device__ __forceinline__ void tile(WaveState<D>& w, const char* stage, const Offsets<D>& o,
                                      const bf16x8 (&qf)[Geo<D>::DCH], float c2, bool masked, int kv0,
-                                     int kv_len, int qrow, int hl) {
+                                     int kv_len, int qrow, int hl, bool first) {
     constexpr int KBLK = Geo<D>::KBLK;
     f32x16 s[2];
     uint32_t pb[2][8];
@@ -300,7 +300,7 @@ __device__ __forceinline__ void tile(WaveState<D>& w, const char* stage, const O
         if (MODE == 2) {
             softmax_block_exact<D>(sb, pb[blk & 1], w, c2);
         } else {
-            if (MODE == 0 && blk == 0) {
+            if (MODE == 3 && blk == 0 && first) {
                 float mx = kNegInf;
 #pragma unroll
                 for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sb[r], sb[r + 1]));
@@ -399,54 +399,55 @@ __device__ __forceinline__ void attend_tile(const Params& p, const Tile& t, cons
         // Iteration j computes on stage j & 1 while the group's next tile is
         // loaded into the other stage; the barrier closing the iteration
         // makes that stage visible and frees stage j & 1 for the load after.
-        // MODE 0: the group's first tile; 1 (fast): every tile is unmasked
-        // for every wave; 3: reference kept, tiles masked where needed;
-        // 2: exact running-max update (the retry pass).
-        auto run = [&](auto mode_tag, int j0, int j1) __attribute__((always_inline)) {
+        // MODE 1 (fast): every tile is unmasked for every wave; 3: reference
+        // kept, tiles masked where needed, the reference set on the group's
+        // first tile; 2: exact running-max update (the retry pass).
+        auto step = [&](auto mode_tag, int j, const char* cur, char* next) __attribute__((always_inline)) {
             constexpr int MODE = decltype(mode_tag)::value;
-            constexpr bool FAST = MODE == 1;
-            // iteration j: compute on `cur` (stage j & 1), load into `next`
-            auto step = [&](int j, const char* cur, char* next) __attribute__((always_inline)) {
-                const int it = KSPLIT * j + grp;
-                const int kv0 = it * BC;
-                if (it + KSPLIT < ntiles) load_tile<D>(o, next, kb, vb, kv0 + KSPLIT * BC, kv_len, wave);
-                if (FAST) {
-                    tile<D, CAUSAL, 1>(w, cur, o, qf, c2, false, kv0, kv_len, qrow, hl);
-                } else if (it < ntiles && !(CAUSAL && kv0 > q0w + 31)) {
-                    // (under a causal mask a wave whose rows all precede the tile skips it)
-                    const bool masked = (kv0 + BC > kv_len) || (CAUSAL && kv0 + BC - 1 > q0w);
-                    tile<D, CAUSAL, MODE>(w, cur, o, qf, c2, masked, kv0, kv_len, qrow, hl);
-                }
-                wait_loads();
-                __syncthreads();
-            };
-            // The fast loop is unrolled by two so that every access names
-            // its stage object: the compiler can then tell the loads into one
-            // stage from the reads of the other and does not wait on the
-            // former for the latter.  The other modes (the first tile, masked
-            // tiles, the retry pass) are rare; they keep one copy of the code
-            // and accept that wait.
-            if constexpr (MODE == 1) {
-                int j = j0;
-                if ((j & 1) && j < j1) step(j++, S1, S0);
-                for (; j < j1; j += 2) {
-                    step(j, S0, S1);
-                    if (j + 1 < j1) step(j + 1, S1, S0);
-                }
-            } else {
-                for (int j = j0; j < j1; ++j) step(j, (j & 1) ? S1 : S0, (j & 1) ? S0 : S1);
+            const int it = KSPLIT * j + grp;
+            const int kv0 = it * BC;
+            if (it + KSPLIT < ntiles) load_tile<D>(o, next, kb, vb, kv0 + KSPLIT * BC, kv_len, wave);
+            if (MODE == 1) {
+                tile<D, CAUSAL, 1>(w, cur, o, qf, c2, false, kv0, kv_len, qrow, hl, false);
+            } else if (it < ntiles && !(CAUSAL && kv0 > q0w + 31)) {
+                // (under a causal mask a wave whose rows all precede the tile skips it)
+                const bool masked = (kv0 + BC > kv_len) || (CAUSAL && kv0 + BC - 1 > q0w);
+                tile<D, CAUSAL, MODE>(w, cur, o, qf, c2, masked, kv0, kv_len, qrow, hl, j == 0);
             }
+            wait_loads();
+            __syncthreads();
+        };
+        // One copy of the code for the rare iterations (first tile, masked
+        // tiles, the retry pass); it names the stages through a select, so
+        // the compiler waits for the next tile's loads before reading.
+        auto run_any = [&](auto mode_tag, int j0, int j1) __attribute__((always_inline)) {
+            for (int j = j0; j < j1; ++j) step(mode_tag, j, (j & 1) ? S1 : S0, (j & 1) ? S0 : S1);
+        };
+        // The fast loop from odd j0, two iterations at a time, so that every
+        // access names its stage object: the compiler then tells the loads
+        // into one stage from the reads of the other and does not wait on
+        // them.  Returns the first iteration it did not run.
+        auto run_fast = [&](int j0, int j1) __attribute__((always_inline)) {
+            int j = j0;
+            for (; j + 1 < j1; j += 2) {
+                step(std::integral_constant<int, 1>{}, j, S1, S0);
+                step(std::integral_constant<int, 1>{}, j + 1, S0, S1);
+            }
+            return j;
         };
         // Tiles before n_full are unmasked for every wave of the workgroup;
         // iterations before j_full only touch such tiles in every group.
         const int n_full = min(ntiles, (CAUSAL ? min(q0, kv_len) : kv_len) / BC);
         if (exact_all) {
-            run(std::integral_constant<int, 2>{}, 0, niters);
+            run_any(std::integral_constant<int, 2>{}, 0, niters);
         } else {
-            const int j_full = n_full / KSPLIT;
-            run(std::integral_constant<int, 0>{}, 0, min(1, niters));
-            run(std::integral_constant<int, 1>{}, 1, j_full);
-            run(std::integral_constant<int, 3>{}, max(1, j_full), niters);
+            // the first tile, then the fast pairs, then the rest; one loop so
+            // that the first tile's masks are not specialised (and kept in
+            // registers) for its constant key offset
+            for (int j = 0; j < niters;) {
+                run_any(std::integral_constant<int, 3>{}, j, j + 1);
+                j = (j == 0) ? run_fast(1, n_full / KSPLIT) : j + 1;
+            }
         }
         if (exact_all) break;
         // overflow check: ℓ and every Oᵀ entry finite (inf · 0 and NaN · 0 are NaN)
