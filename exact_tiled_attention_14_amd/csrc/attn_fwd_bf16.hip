@@ -265,10 +265,17 @@ __device__ __forceinline__ void qk_block(f32x16& s, const char* ks, const Offset
                                          const bf16x8 (&qf)[Geo<D>::DCH], int blk) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.f;
+    uint4 a[Geo<D>::DCH];
 #pragma unroll
-    for (int c = 0; c < Geo<D>::DCH; ++c) {
-        const uint4 a = *reinterpret_cast<const uint4*>(ks + o.k_rd + blk * 32 * Cfg<D>::KROW + c * 32);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[c], s, 0, 0, 0);
+    for (int c = 0; c < Geo<D>::DCH; ++c) a[c] = *reinterpret_cast<const uint4*>(ks + o.k_rd + blk * 32 * Cfg<D>::KROW + c * 32);
+#pragma unroll
+    for (int c = 0; c < Geo<D>::DCH; ++c)
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[c]), qf[c], s, 0, 0, 0);
+    if (blk == 0) {
+        // a tile's first block has no other work to hide the LDS latency
+        // behind: issue all its operand reads before its MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, Geo<D>::DCH, 0);  // LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, Geo<D>::DCH, 0);  // MFMAs
     }
 }
 
