@@ -10,12 +10,15 @@ no attention arithmetic) or from the tests themselves.
 Every function here is pinned by a ``-m "not gpu"`` test in ``tests/`` against
 something other than itself (closed forms, invariants, a library routine,
 brute force over every block size); see ``tests/test_oracle_pins.py`` and
-``tests/test_oracle_blockwise.py``.  No function here is "parity unpinned".
+``tests/test_oracle_blockwise.py``; the backward pass against torch autograd,
+finite differences and invariants in ``tests/test_oracle_backward.py``.  No
+function here is "parity unpinned".
 """
 
 from .attention import (  # noqa: F401
     admissible,
     attention,
+    attention_backward,
     blockwise_attention,
     kv_head_of,
     merge_partials,

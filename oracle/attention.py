@@ -38,6 +38,7 @@ __all__ = [
     "blockwise_attention",
     "merge_partials",
     "merge_softmax",
+    "attention_backward",
 ]
 
 
@@ -212,3 +213,52 @@ def merge_softmax(x, y):
     wy = np.exp(my - m) * ly
     ell = wx + wy
     return np.concatenate([wx[:, None] * px, wy[:, None] * py], axis=1)[0] / ell[0]
+
+
+def attention_backward(q, k, v, dout, scale, causal=False, key_lens=None):
+    """Gradients of the loss L = Σ O ∘ dO through exact attention.
+
+    The pages only say that the tiled method recomputes the attention weights
+    in the backward pass instead of storing them (unite.ai page, section
+    "闪电注意力的到来", key idea 2) and that FlashAttention-2 speeds the backward
+    pass up (section "闪电注意力-2"); the gradients themselves are those of the
+    definition above, written out by the chain rule (a reading), for each
+    (b, h) with g = its kv head and A the admissible keys:
+
+        P = softmax(S) with S = scale·Q Kᵀ over A,   O = P V
+        dV_g += Pᵀ dO
+        dP    = dO Vᵀ
+        D_i   = Σ_j P_ij dP_ij   (= Σ_d dO_i,d O_i,d)
+        dS    = P ∘ (dP − D)     (the softmax Jacobian applied to dP)
+        dQ    = scale · dS K
+        dK_g += scale · dSᵀ Q
+
+    q, dout: [B, H, N, d]; k, v: [B, Hkv, N, d]; key_lens as in
+    ``attention``.  Returns fp64 (dQ [B, H, N, d], dK [B, Hkv, N, d],
+    dV [B, Hkv, N, d]).  Padded keys (j ≥ key_len) get dK = dV = 0; a row
+    with no admissible key contributes nothing.
+    """
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    assert k.shape == (B, Hkv, N, d) and v.shape == k.shape and dout.shape == q.shape
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    rows = np.arange(N)
+    for b in range(B):
+        kl = N if key_lens is None else int(min(max(int(key_lens[b]), 0), N))
+        for h in range(H):
+            g = kv_head_of(h, H, Hkv)
+            kv_k, kv_v = k[b, g, :kl], v[b, g, :kl]
+            s = scores(q[b, h], kv_k, scale)
+            s = np.where(admissible(rows, kl, causal), s, -np.inf)
+            p, _, _ = softmax_rows(s)
+            do = dout[b, h]
+            dv[b, g, :kl] += p.T @ do
+            dp = do @ kv_v.T
+            D = (p * dp).sum(axis=1)
+            ds = p * (dp - D[:, None])
+            dq[b, h] = scale * (ds @ kv_k)
+            dk[b, g, :kl] += scale * (ds.T @ q[b, h])
+    return dq, dk, dv
