@@ -1,11 +1,12 @@
-"""Python binding of the MI355X exact tiled attention forward library.
+"""Python binding of the MI355X exact tiled attention library.
 
 Thin ctypes layer over ``libattn.so`` (see ``include/attn.h``): the functions
-``attn_fwd_bf16``, ``attn_fwd_f32``, ``attn_fwd`` and ``attn_status_str`` take
-the same arguments as the C entry points (device pointers as Python ints) and
-return the status code.  ``forward`` marshals torch tensors onto them; every
-step of the computation runs in the HIP kernels.  There is no fallback: if
-the library is missing, every call raises.
+``attn_fwd_bf16``, ``attn_fwd_f32``, ``attn_fwd``, ``attn_bwd_bf16`` and
+``attn_status_str`` take the same arguments as the C entry points (device
+pointers as Python ints) and return the status code.  ``forward`` and
+``backward`` marshal torch tensors onto them; every step of the computation
+runs in the HIP kernels.  There is no fallback: if the library is missing,
+every call raises.
 """
 
 import ctypes
@@ -13,8 +14,8 @@ import math
 import os
 
 __all__ = [
-    "AttnError", "attn_fwd", "attn_fwd_bf16", "attn_fwd_f32", "attn_status_str",
-    "forward", "library_path", "load_library",
+    "AttnError", "attn_fwd", "attn_fwd_bf16", "attn_fwd_f32", "attn_bwd_bf16", "attn_status_str",
+    "forward", "backward", "library_path", "load_library",
     "ATTN_OK", "ATTN_ERR_NULL", "ATTN_ERR_SHAPE", "ATTN_ERR_HEAD_DIM", "ATTN_ERR_ALIGN",
     "ATTN_ERR_SCALE", "ATTN_ERR_HIP",
 ]
@@ -33,6 +34,7 @@ ENTRY_POINTS = {
     "attn_fwd_bf16": (_FWD_ARGS, ctypes.c_int),
     "attn_fwd_f32": (_FWD_ARGS, ctypes.c_int),
     "attn_fwd": (_FWD_ARGS, ctypes.c_int),
+    "attn_bwd_bf16": ([_P] * 10 + [_I, _I, _I, _I, _I, ctypes.c_float, _I, _P, _P], ctypes.c_int),
     "attn_status_str": ([_I], ctypes.c_char_p),
 }
 
@@ -79,6 +81,11 @@ def attn_fwd(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, key_lens, stream):
     return load_library().attn_fwd(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, key_lens, stream)
 
 
+def attn_bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, Hkv, N, d, scale, causal, key_lens, stream):
+    return load_library().attn_bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, delta,
+                                        B, H, Hkv, N, d, scale, causal, key_lens, stream)
+
+
 def attn_status_str(status):
     return load_library().attn_status_str(int(status)).decode()
 
@@ -123,3 +130,39 @@ def forward(q, k, v, *, scale=None, causal=False, key_lens=None, out=None, lse=N
     if st != ATTN_OK:
         raise AttnError(st, fn.__name__)
     return out, lse
+
+
+def backward(q, k, v, o, lse, dout, *, scale=None, causal=False, key_lens=None, stream=None):
+    """Gradients (dq, dk, dv) of sum(o * dout) for bf16 GPU tensors, where
+    (o, lse) = forward(q, k, v, ...) with the same arguments.  Allocates the
+    outputs and the fp32 [B, H, N] D buffer; the two kernels are enqueued on
+    ``stream`` (default: torch's current stream) and not waited on."""
+    import torch
+
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bfloat16 GPU tensor")
+    if tuple(k.shape) != (B, Hkv, N, d) or tuple(v.shape) != tuple(k.shape) or o.shape != q.shape \
+            or dout.shape != q.shape or tuple(lse.shape) != (B, H, N) or lse.dtype != torch.float32:
+        raise ValueError("shape or dtype mismatch")
+    if key_lens is not None:
+        if key_lens.dtype != torch.int32 or not key_lens.is_cuda or key_lens.numel() != B:
+            raise ValueError("key_lens must be an int32 GPU tensor with B entries")
+        key_lens = key_lens.contiguous()
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = attn_bwd_bf16(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                       dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+                       B, H, Hkv, N, d, float(scale), int(bool(causal)),
+                       key_lens.data_ptr() if key_lens is not None else None, stream)
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_bwd_bf16")
+    return dq, dk, dv

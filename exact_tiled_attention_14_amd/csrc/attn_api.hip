@@ -10,6 +10,7 @@
 namespace attn {
 hipError_t launch_fwd_bf16(const Params& p, int d, bool causal, const Schedule& sc, hipStream_t stream);
 hipError_t launch_fwd_f32(const Params& p, int d, bool causal, hipStream_t stream);
+hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool causal, hipStream_t stream);
 }  // namespace attn
 
 namespace {
@@ -116,6 +117,29 @@ int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float
     if (st != ATTN_OK || empty) return st;
     (void)hipGetLastError();
     const hipError_t e = attn::launch_fwd_f32(p, d, causal != 0, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                  void* dq, void* dk, void* dv, float* delta,
+                  int B, int H, int Hkv, int N, int d, float scale, int causal,
+                  const int32_t* key_lens, void* stream) {
+    attn::BwdParams bp;
+    bool empty = false;
+    const int st = validate(q, k, v, dq, lse, B, H, Hkv, N, d, scale, causal, key_lens, &bp.f, &empty);
+    if (st != ATTN_OK || empty) return st;
+    if (!o || !dout || !dk || !dv || !delta) return ATTN_ERR_NULL;
+    if (!aligned16(o) || !aligned16(dout) || !aligned16(dk) || !aligned16(dv) || !aligned16(delta))
+        return ATTN_ERR_ALIGN;
+    bp.o = o;
+    bp.dout = dout;
+    bp.dq = dq;
+    bp.dk = dk;
+    bp.dv = dv;
+    bp.delta = delta;
+    bp.scale = scale;
+    (void)hipGetLastError();
+    const hipError_t e = attn::launch_bwd_bf16(bp, d, causal != 0, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

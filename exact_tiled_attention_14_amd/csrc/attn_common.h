@@ -35,6 +35,19 @@ struct Params {
                         // every score is 0, computed as q = 0 with c = 1
 };
 
+// Backward pass: the forward's problem (q, k, v, lse, sizes, key_lens) plus
+// the forward output, its gradient, the three gradients and the D buffer.
+struct BwdParams {
+    Params f;
+    const void* o;
+    const void* dout;
+    void* dq;
+    void* dk;
+    void* dv;
+    float* delta;  // [B][H][N] fp32: D_i = Σ_d dO_i,d O_i,d (written, then read)
+    float scale;   // as passed (any finite value)
+};
+
 // Launch shape chosen on the host: key-range split (1 or 2 wave groups),
 // persistent causal schedule, number of workgroups.
 struct Schedule {

@@ -69,6 +69,27 @@ int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float
                  int B, int H, int Hkv, int N, int d, float scale, int causal,
                  const int32_t* key_lens, void* stream);
 
+/* Backward pass, bf16 (gradients of L = Σ O ∘ dout through the operation
+ * above; the attention weights are recomputed from q, k and the forward's lse
+ * rather than stored: unite.ai page "闪电注意力：革命性地提高Transformer效率",
+ * section "闪电注意力的到来", key idea 2):
+ *     P = exp(scale·q kᵀ − lse) on the admissible keys, D_i = Σ_d dout_i,d o_i,d,
+ *     dS = P ∘ (dout vᵀ − D),  dq = scale·dS k,  dk = scale·dSᵀ q,  dv = Pᵀ dout,
+ * with the grouped query heads of a kv head adding into its dk and dv.
+ * Inputs q, k, v, o, dout (bf16) and lse (fp32) in the layouts above; o and lse
+ * must be this library's forward results for the same arguments.  Outputs
+ * dq [B][H][N][d], dk, dv [B][Hkv][N][d] (bf16, every element written; padded
+ * keys get 0).  delta: caller-owned fp32 [B][H][N] scratch, overwritten with D.
+ * Products on bf16 matrix cores with fp32 accumulation; P and dS are rounded
+ * to bf16 as operands.  Any finite scale.  Two kernels are enqueued on
+ * `stream` in order; same validation and status codes as attn_fwd_bf16 (q, k,
+ * v, dq and lse are checked as its q, k, v, o and lse; then o, dout, dk, dv,
+ * delta for NULL and alignment).  Outputs must not overlap the inputs. */
+int attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                  void* dq, void* dk, void* dv, float* delta,
+                  int B, int H, int Hkv, int N, int d, float scale, int causal,
+                  const int32_t* key_lens, void* stream);
+
 /* The hot path: identical to attn_fwd_bf16. */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int H, int Hkv, int N, int d, float scale, int causal,

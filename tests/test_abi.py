@@ -103,3 +103,37 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(attn, "library_path", lambda: str(tmp_path / "nope.so"))
     with pytest.raises(RuntimeError, match="no fallback"):
         attn.load_library()
+
+
+BWD_GOOD = dict(q=P, k=P * 2, v=P * 3, o=P * 4, dout=P * 5, lse=P * 6, dq=P * 7, dk=P * 8, dv=P * 9,
+                delta=P * 10, B=1, H=4, Hkv=2, N=64, d=128, scale=0.125, causal=1, key_lens=None, stream=None)
+
+
+def call_bwd(**over):
+    a = dict(BWD_GOOD, **over)
+    return attn.attn_bwd_bf16(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["dq"], a["dk"], a["dv"],
+                              a["delta"], a["B"], a["H"], a["Hkv"], a["N"], a["d"], a["scale"], a["causal"],
+                              a["key_lens"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(d=96), attn.ATTN_ERR_HEAD_DIM),
+    (dict(H=3, Hkv=2), attn.ATTN_ERR_SHAPE),
+    (dict(causal=-1), attn.ATTN_ERR_SHAPE),
+    (dict(scale=math.inf), attn.ATTN_ERR_SCALE),
+    (dict(q=None), attn.ATTN_ERR_NULL),
+    (dict(dq=None), attn.ATTN_ERR_NULL),
+    (dict(lse=None), attn.ATTN_ERR_NULL),
+    (dict(o=None), attn.ATTN_ERR_NULL),
+    (dict(dout=None), attn.ATTN_ERR_NULL),
+    (dict(dk=None), attn.ATTN_ERR_NULL),
+    (dict(dv=None), attn.ATTN_ERR_NULL),
+    (dict(delta=None), attn.ATTN_ERR_NULL),
+    (dict(dout=P + 8), attn.ATTN_ERR_ALIGN),
+    (dict(dv=P + 2), attn.ATTN_ERR_ALIGN),
+    (dict(delta=P + 4), attn.ATTN_ERR_ALIGN),
+    (dict(B=0, q=None, k=None, v=None, o=None, dout=None, lse=None, dq=None, dk=None, dv=None, delta=None),
+     attn.ATTN_OK),
+])
+def test_backward_host_validation(over, status):
+    assert call_bwd(**over) == status

@@ -1,0 +1,107 @@
+"""GPU parity of the backward pass (attn_bwd_bf16 through the C ABI) against
+the fp64 backward oracle, on bf16 inputs.
+
+Tolerance: max |grad_gpu − grad_oracle| ≤ 2e-2 · max |grad_oracle| per tensor
+(dQ, dK, dV).  The gradients are stored in bf16 (relative rounding 2^-9), and
+inside the kernels P and dS are rounded to bf16 as matrix-core operands and D
+is formed from the bf16 forward output; each of these is a relative
+perturbation of order 2^-9 of terms that are summed over up to N keys or
+queries with mixed signs, so the bound leaves a margin of about 10× over
+2^-9 on the largest gradient entry.  No NaN may appear.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import exact_tiled_attention_14_amd as attn
+import oracle
+from workloads import as_f64
+
+pytestmark = pytest.mark.gpu
+
+TOL_REL = 2e-2
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    attn.load_library()
+    return torch.device("cuda:0")
+
+
+def _inputs(B, H, Hkv, N, d, seed):
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn(B, H, N, d, generator=g).to(torch.bfloat16)
+    k = torch.randn(B, Hkv, N, d, generator=g).to(torch.bfloat16)
+    v = torch.randn(B, Hkv, N, d, generator=g).to(torch.bfloat16)
+    do = torch.randn(B, H, N, d, generator=g).to(torch.bfloat16)
+    return q, k, v, do
+
+
+def run_case(dev, B, H, Hkv, N, d, causal, key_lens, seed, scale=None, poison=False):
+    what = f"bwd B{B} H{H} Hkv{Hkv} N{N} d{d} causal={causal} key_lens={key_lens} scale={scale}"
+    print(what, flush=True)
+    q, k, v, do = _inputs(B, H, Hkv, N, d, seed)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    scale = float(np.float32(scale))
+    kl = None if key_lens is None else torch.tensor(key_lens, dtype=torch.int32)
+    kg, vg = k.clone(), v.clone()
+    if poison and key_lens is not None:
+        for b, n in enumerate(key_lens):
+            kg[b, :, max(n, 0):] = float("nan")
+            vg[b, :, max(n, 0):] = float("nan")
+    qd, kd, vd, dod = (t.to(dev).contiguous() for t in (q, kg, vg, do))
+    kld = None if kl is None else kl.to(dev)
+    o, lse = attn.forward(qd, kd, vd, scale=scale, causal=causal, key_lens=kld)
+    dq, dk, dv = attn.backward(qd, kd, vd, o, lse, dod, scale=scale, causal=causal, key_lens=kld)
+    torch.cuda.synchronize()
+    ref = oracle.attention_backward(as_f64(q), as_f64(k), as_f64(v), as_f64(do), scale, causal=causal,
+                                    key_lens=key_lens)
+    for name, got, want in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
+        g64 = as_f64(got.cpu())
+        assert not np.isnan(g64).any(), f"{what}: NaN in {name}"
+        err = float(np.max(np.abs(g64 - want))) if want.size else 0.0
+        mag = float(np.max(np.abs(want))) if want.size else 0.0
+        print(f"  {name}: max err {err:.3e}  max |ref| {mag:.3e}", flush=True)
+        assert err <= TOL_REL * mag + 1e-6, f"{what}: {name} max err {err:.3e} > {TOL_REL} x {mag:.3e}"
+    return dq, dk, dv
+
+
+SMALL = [  # (B, H, Hkv, N, d): ragged tails, several tiles, grouped heads
+    (1, 1, 1, 1, 64), (2, 2, 1, 17, 64), (1, 4, 2, 100, 128), (2, 2, 2, 129, 64),
+    (1, 2, 1, 255, 128), (1, 3, 3, 300, 64), (2, 4, 2, 200, 128),
+]
+
+
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "B{}H{}Hkv{}N{}d{}".format(*s))
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_small(dev, shape, causal):
+    B, H, Hkv, N, d = shape
+    run_case(dev, B, H, Hkv, N, d, causal, None, seed=7 + N)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_padded_with_poison(dev, causal, d):
+    # padded K/V hold NaN: they must not reach any gradient; padded keys get 0
+    N = 190
+    key_lens = [150, 0, 190, 1]
+    dq, dk, dv = run_case(dev, 4, 2, 1, N, d, causal, key_lens, seed=11, poison=True)
+    dk, dv = as_f64(dk.cpu()), as_f64(dv.cpu())
+    for b, n in enumerate(key_lens):
+        assert np.all(dk[b, :, n:] == 0) and np.all(dv[b, :, n:] == 0), "padded keys"
+    assert np.all(as_f64(dq.cpu())[1] == 0), "sequence without keys"
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.2])
+def test_backward_scale_edge_cases(dev, scale):
+    run_case(dev, 1, 2, 1, 70, 64, True, None, seed=13, scale=scale)
+
+
+def test_backward_medium(dev):
+    # several query and key tiles in both kernels, grouped heads, causal
+    run_case(dev, 1, 4, 2, 700, 128, True, None, seed=17)
