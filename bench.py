@@ -105,19 +105,45 @@ class Runner:
         if st != 0:
             raise RuntimeError(f"attention launch failed with status {st}")
 
-    def time(self, steps, warmup):
+    def prepare_backward(self):
+        """Forward outputs, a seeded dout and the gradient buffers (bf16 only)."""
+        import torch
+
+        import exact_tiled_attention_14_amd as attn
+
+        w = self.w
+        self.launch()
+        g = torch.Generator().manual_seed(1000 + w.seed)
+        self.dout = torch.randn(self.q.shape, generator=g).to(torch.bfloat16).to(self.q.device)
+        self.dq = torch.empty_like(self.q)
+        self.dk = torch.empty_like(self.k)
+        self.dv = torch.empty_like(self.v)
+        self.delta = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=self.q.device)
+        self.bwd_args = (self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), self.o.data_ptr(),
+                         self.dout.data_ptr(), self.lse.data_ptr(), self.dq.data_ptr(), self.dk.data_ptr(),
+                         self.dv.data_ptr(), self.delta.data_ptr(), w.B, w.H, w.Hkv, w.N, w.d, w.scale,
+                         int(w.causal), None if self.kl is None else self.kl.data_ptr(), self.stream.cuda_stream)
+        self.bwd_fn = attn.attn_bwd_bf16
+
+    def launch_backward(self):
+        st = self.bwd_fn(*self.bwd_args)
+        if st != 0:
+            raise RuntimeError(f"backward launch failed with status {st}")
+
+    def time(self, steps, warmup, fn=None):
         """Average milliseconds per launch over `steps` back-to-back launches,
         bracketed by HIP events recorded on the launch stream."""
         import torch
 
+        fn = fn or self.launch
         for _ in range(warmup):
-            self.launch()
+            fn()
         torch.cuda.synchronize()
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
         start.record(self.stream)
         for _ in range(steps):
-            self.launch()
+            fn()
         end.record(self.stream)
         torch.cuda.synchronize()
         return start.elapsed_time(end) / steps
@@ -174,6 +200,7 @@ def main():
     ap.add_argument("--workload", type=int, default=HEADLINE)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip timing the other bf16 workloads")
+    ap.add_argument("--no-backward", action="store_true", help="skip timing the backward pass")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 3 device-to-device copies of MIB MiB (a plain copy kernel of known "
                          "traffic, to calibrate the FETCH_SIZE / WRITE_SIZE counters)")
@@ -252,6 +279,25 @@ def main():
             }
             del rr
         line["workloads"] = extra
+
+    if not args.no_backward:
+        # backward pass (dq, dk, dv): algorithmic flops = 2.5 x the forward's
+        # (five products per admissible (query, key) pair instead of two)
+        bwd = {}
+        for wid in (2, 3, 4, 5):
+            ww = WORKLOADS[wid]
+            if ww.dtype != "bf16":
+                continue
+            rr = Runner(ww, dev)
+            rr.prepare_backward()
+            steps = max(5, min(args.steps, 30))
+            m = rr.time(steps, 3, fn=rr.launch_backward)
+            a = 2.5 * algorithmic_flops(ww, rr.key_lens_host)
+            bwd[str(wid)] = {"workload": ww.name, "ms": round(m, 4), "steps": steps,
+                             "algorithmic_tflops": round(a / (m * 1e-3) / 1e12, 2),
+                             "frac_of_bf16_peak": round(a / (m * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+            del rr
+        line["backward"] = bwd
 
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
