@@ -283,7 +283,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdParams p) {
 // dK, dV
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void attn_bwd_dkv_kernel(BwdParams p) {
+__global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkv_kernel(BwdParams p) {
     using G = BwdGeo<D>;
     constexpr int STAGE = 2 * G::T_ALLOC + 2048;  // Q tile, dO tile, LSE, D
     __shared__ __attribute__((aligned(16))) char s0[STAGE];
@@ -367,6 +367,9 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void attn_bwd_dkv_kerne
         const char* dos = cur + G::T_ALLOC;
         const float* lse_s = reinterpret_cast<const float*>(cur + 2 * G::T_ALLOC);
         const float* d_s = reinterpret_cast<const float*>(cur + 2 * G::T_ALLOC + 1024);
+        // masks are needed only where the tile passes the sequence end, the
+        // key length or (causal) the diagonal
+        const bool masked = (r0 + G::TILE > N) || (k0 + kBR > kv_len) || (CAUSAL && k0 + kBR - 1 > r0);
         // under a causal mask a wave whose keys all follow the tile's rows skips it
         if (!(CAUSAL && k0 + wave * 32 > r0 + G::TILE - 1)) {
 #pragma unroll
@@ -381,33 +384,34 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 1 : 2) void attn_bwd_dkv_kerne
                     const uint4 b2 = *reinterpret_cast<const uint4*>(dos + a_rd + qb * 32 * G::ROW + c * 32);
                     dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, b2), vf[c], dp, 0, 0, 0);
                 }
-                // register r of half h: query r0 + 32 qb + 16 (r / 8) + 8h + r % 8
-                float lse_r[16], d_r[16];
+                // register r of half h: query r0 + 32 qb + 16 (r / 8) + 8h + r % 8;
+                // every row with a key here has a finite LSE (key 0 is admissible)
+                uint32_t pb[8], dsb[8];
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
                     const float4* lp = reinterpret_cast<const float4*>(lse_s + qb * 32 + 16 * hh + 8 * hl);
                     const float4* dq = reinterpret_cast<const float4*>(d_s + qb * 32 + 16 * hh + 8 * hl);
                     const float4 l0 = lp[0], l1 = lp[1], e0 = dq[0], e1 = dq[1];
-                    lse_r[8 * hh + 0] = l0.x; lse_r[8 * hh + 1] = l0.y; lse_r[8 * hh + 2] = l0.z; lse_r[8 * hh + 3] = l0.w;
-                    lse_r[8 * hh + 4] = l1.x; lse_r[8 * hh + 5] = l1.y; lse_r[8 * hh + 6] = l1.z; lse_r[8 * hh + 7] = l1.w;
-                    d_r[8 * hh + 0] = e0.x; d_r[8 * hh + 1] = e0.y; d_r[8 * hh + 2] = e0.z; d_r[8 * hh + 3] = e0.w;
-                    d_r[8 * hh + 4] = e1.x; d_r[8 * hh + 5] = e1.y; d_r[8 * hh + 6] = e1.z; d_r[8 * hh + 7] = e1.w;
-                }
-                uint32_t pb[8], dsb[8];
+                    const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+                    const float dv8[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
 #pragma unroll
-                for (int r = 0; r < 16; r += 2) {
-                    float pe[2], de[2];
+                    for (int u = 0; u < 8; u += 2) {
+                        float pe[2], de[2];
 #pragma unroll
-                    for (int u = 0; u < 2; ++u) {
-                        const int q = r0 + qb * 32 + 16 * ((r + u) >> 3) + 8 * hl + ((r + u) & 7);
-                        const bool ok = q < N && key < kv_len && (!CAUSAL || key <= q) &&
-                                        lse_r[r + u] != -__builtin_inff();
-                        const float pr = ok ? exp2_fast(__builtin_fmaf(s[r + u], c2, -lse_r[r + u] * kLog2e)) : 0.f;
-                        pe[u] = pr;
-                        de[u] = pr * (dp[r + u] - d_r[r + u]);
+                        for (int w2 = 0; w2 < 2; ++w2) {
+                            const int r = 8 * hh + u + w2;
+                            float pr = exp2_fast(__builtin_fmaf(s[r], c2, -lv[u + w2] * kLog2e));
+                            if (masked) {
+                                const int q = r0 + qb * 32 + 16 * hh + 8 * hl + u + w2;
+                                const bool ok = q < N && key < kv_len && (!CAUSAL || key <= q);
+                                pr = ok ? pr : 0.f;
+                            }
+                            pe[w2] = pr;
+                            de[w2] = pr * (dp[r] - dv8[u + w2]);
+                        }
+                        pb[(8 * hh + u) >> 1] = pack2(pe[0], pe[1]);
+                        dsb[(8 * hh + u) >> 1] = pack2(de[0], de[1]);
                     }
-                    pb[r >> 1] = pack2(pe[0], pe[1]);
-                    dsb[r >> 1] = pack2(de[0], de[1]);
                 }
                 // dVᵀ += dOᵀ · P,  dKᵀ += Qᵀ · dS
 #pragma unroll
