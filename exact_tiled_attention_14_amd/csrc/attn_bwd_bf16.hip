@@ -294,12 +294,24 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkv_kernel(BwdParams p) 
     const int lane = tid & 63, hl = lane >> 5, ql = lane & 31;
     const int N = p.f.N, H = p.f.H, Hkv = p.f.Hkv, GR = H / Hkv;
 
-    // workgroup -> (kv head g, batch b, key tile kt); key tile 0 (the most
-    // query tiles under a causal mask) first
+    // workgroup -> (kv head g, batch b, key tile kt).  The hardware deals
+    // workgroup ids round-robin over the 8 XCDs; each XCD gets a contiguous
+    // range of (g, b) heads (whose Q and dO its L2 then serves to all their
+    // key tiles) and walks it key tile by key tile, lowest first: under a
+    // causal mask key tile 0 sees the most query rows, so the longest work
+    // is issued first.
     const int ktiles = (N + kBR - 1) / kBR;
-    const int wg = blockIdx.x;
-    const int kt = wg % ktiles;
-    const int bg = wg / ktiles;
+    const int heads = p.f.B * Hkv;
+    int bg, kt;
+    if (heads % kXcds == 0) {  // then every XCD holds heads/8 heads × ktiles workgroups
+        const int x = blockIdx.x % kXcds, k = blockIdx.x / kXcds;
+        const int nh = heads / kXcds;
+        kt = k / nh;
+        bg = x * nh + k % nh;
+    } else {
+        kt = blockIdx.x / heads;
+        bg = blockIdx.x % heads;
+    }
     const int g = bg / p.f.B, b = bg - g * p.f.B;
     const int k0 = kt * kBR;
     const int key = k0 + wave * 32 + ql;  // this lane's key (B-operand column)
