@@ -74,7 +74,8 @@ int device_cus() {
 // workgroups, one per CU with two wave groups each, are dealt a balanced
 // (zig-zag, longest first) list.  Otherwise one workgroup per query tile,
 // issued longest first; the key range is split over two wave groups when the
-// grid has fewer than two workgroups per CU.
+// grid has fewer than two workgroups per CU.  (At d = 64 one workgroup needs
+// few enough registers and LDS for three per CU when the grid is large.)
 attn::Schedule schedule_bf16(const attn::Params& p, bool causal) {
     const int64_t items = (int64_t)p.B * p.H * p.q_tiles;
     const int cus = device_cus();

@@ -75,7 +75,7 @@ struct Cfg<128> {
 
 template <>
 struct Cfg<64> {
-    static constexpr int BC = 128;
+    static constexpr int BC = 64;
     static constexpr int KROW = 64 * 2 + 16;
     static constexpr int VROW = 64 * 2;
     static constexpr int K_BYTES = BC * KROW;
@@ -550,7 +550,7 @@ __device__ __forceinline__ bool persistent_item(const Params& p, int i, Tile* t)
 }
 
 template <int D, bool CAUSAL, int KSPLIT, bool PERSIST>
-__global__ __launch_bounds__(kThreads * KSPLIT, 2 / KSPLIT) void attn_fwd_bf16_kernel(Params p) {
+__global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT == 1 ? (D == 64 ? 3 : 2) : 1) void attn_fwd_bf16_kernel(Params p) {
     __shared__ __attribute__((aligned(16))) char s0[KSPLIT * Geo<D>::STAGE];
     __shared__ __attribute__((aligned(16))) char s1[KSPLIT * Geo<D>::STAGE];
     const Lds<D, KSPLIT> lds{s0, s1};
