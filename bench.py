@@ -17,7 +17,6 @@ pairs) rates and their fraction of the bf16 MFMA peak.
 """
 
 import argparse
-import glob
 import hashlib
 import json
 import math
@@ -55,11 +54,15 @@ def algorithmic_bytes(w):
     return (2 * w.B * w.H * w.N * w.d + 2 * w.B * w.Hkv * w.N * w.d) * e + 4 * w.B * w.H * w.N
 
 
+# the sources that decide what the forward bf16 kernel does and how it is launched
+FORWARD_SOURCES = ("attn_api.hip", "attn_common.h", "attn_fwd_bf16.hip")
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "exact_tiled_attention_14_amd", "csrc", "*"))):
-        with open(p, "rb") as f:
-            h.update(os.path.basename(p).encode() + f.read())
+    for name in FORWARD_SOURCES:
+        with open(os.path.join(ROOT, "exact_tiled_attention_14_amd", "csrc", name), "rb") as f:
+            h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
 
 
