@@ -152,6 +152,35 @@ class Runner:
         return start.elapsed_time(end) / steps
 
 
+class VarlenRunner(Runner):
+    """The packed variable-length batch (attn_fwd_varlen_bf16) resident on the GPU."""
+
+    def __init__(self, spec, dev):
+        import torch
+
+        import exact_tiled_attention_14_amd as attn
+        from workloads import make_varlen, varlen_lengths
+
+        self.spec = spec
+        self.lengths = varlen_lengths(spec["B"], spec["N"] // 2, spec["N"], spec["seed"])
+        q, k, v, cu = make_varlen(self.lengths, spec["H"], spec["Hkv"], spec["d"], seed=spec["seed"])
+        total = q.shape[0]
+        self.q, self.k, self.v, self.cu = q.to(dev), k.to(dev), v.to(dev), cu.to(dev)
+        self.o = torch.empty_like(self.q)
+        self.lse = torch.empty((spec["H"], total), dtype=torch.float32, device=dev)
+        self.stream = torch.cuda.current_stream(dev)
+        self.fn = attn.attn_fwd_varlen_bf16
+        scale = float(1.0 / math.sqrt(spec["d"]))
+        self.args = (self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), self.o.data_ptr(),
+                     self.lse.data_ptr(), self.cu.data_ptr(), spec["B"], spec["H"], spec["Hkv"], total,
+                     spec["N"], spec["d"], scale, int(spec["causal"]), self.stream.cuda_stream)
+
+    def algorithmic_flops(self):
+        s = self.spec
+        pairs = sum(n * (n + 1) / 2 if s["causal"] else n * n for n in self.lengths)
+        return 4.0 * s["d"] * s["H"] * pairs
+
+
 def cpu_baseline(w, budget_s=10.0):
     """The fp64 oracle, as it stands, on this host's cores over a bounded sample
     of the workload: whole (b, h) heads, all query rows, in order, repeating
@@ -204,6 +233,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip timing the other bf16 workloads")
     ap.add_argument("--no-backward", action="store_true", help="skip timing the backward pass")
+    ap.add_argument("--no-varlen", action="store_true", help="skip timing the packed variable-length batch")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 3 device-to-device copies of MIB MiB (a plain copy kernel of known "
                          "traffic, to calibrate the FETCH_SIZE / WRITE_SIZE counters)")
@@ -301,6 +331,18 @@ def main():
                              "frac_of_bf16_peak": round(a / (m * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
             del rr
         line["backward"] = bwd
+
+    if not args.no_varlen:
+        from workloads import VARLEN
+
+        vr = VarlenRunner(VARLEN, dev)
+        steps = max(5, min(args.steps, 30))
+        m = vr.time(steps, 3)
+        a = vr.algorithmic_flops()
+        line["varlen"] = {"workload": VARLEN["name"], "lengths": vr.lengths, "ms": round(m, 4), "steps": steps,
+                          "algorithmic_tflops": round(a / (m * 1e-3) / 1e12, 2),
+                          "frac_of_bf16_peak": round(a / (m * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        del vr
 
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)

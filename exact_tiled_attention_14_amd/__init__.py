@@ -1,10 +1,11 @@
 """Python binding of the MI355X exact tiled attention library.
 
 Thin ctypes layer over ``libattn.so`` (see ``include/attn.h``): the functions
-``attn_fwd_bf16``, ``attn_fwd_f32``, ``attn_fwd``, ``attn_bwd_bf16`` and
-``attn_status_str`` take the same arguments as the C entry points (device
-pointers as Python ints) and return the status code.  ``forward`` and
-``backward`` marshal torch tensors onto them; every step of the computation
+``attn_fwd_bf16``, ``attn_fwd_f32``, ``attn_fwd``, ``attn_fwd_varlen_bf16``,
+``attn_bwd_bf16`` and ``attn_status_str`` take the same arguments as the C
+entry points (device pointers as Python ints) and return the status code.
+``forward``, ``forward_varlen`` and ``backward`` marshal torch tensors onto
+them; every step of the computation
 runs in the HIP kernels.  There is no fallback: if the library is missing,
 every call raises.
 """
@@ -14,8 +15,8 @@ import math
 import os
 
 __all__ = [
-    "AttnError", "attn_fwd", "attn_fwd_bf16", "attn_fwd_f32", "attn_bwd_bf16", "attn_status_str",
-    "forward", "backward", "library_path", "load_library",
+    "AttnError", "attn_fwd", "attn_fwd_bf16", "attn_fwd_f32", "attn_fwd_varlen_bf16", "attn_bwd_bf16",
+    "attn_status_str", "forward", "forward_varlen", "backward", "library_path", "load_library",
     "ATTN_OK", "ATTN_ERR_NULL", "ATTN_ERR_SHAPE", "ATTN_ERR_HEAD_DIM", "ATTN_ERR_ALIGN",
     "ATTN_ERR_SCALE", "ATTN_ERR_HIP",
 ]
@@ -34,6 +35,7 @@ ENTRY_POINTS = {
     "attn_fwd_bf16": (_FWD_ARGS, ctypes.c_int),
     "attn_fwd_f32": (_FWD_ARGS, ctypes.c_int),
     "attn_fwd": (_FWD_ARGS, ctypes.c_int),
+    "attn_fwd_varlen_bf16": ([_P] * 6 + [_I] * 6 + [ctypes.c_float, _I, _P], ctypes.c_int),
     "attn_bwd_bf16": ([_P] * 10 + [_I, _I, _I, _I, _I, ctypes.c_float, _I, _P, _P], ctypes.c_int),
     "attn_status_str": ([_I], ctypes.c_char_p),
 }
@@ -79,6 +81,11 @@ def attn_fwd_f32(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, key_lens, stre
 
 def attn_fwd(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, key_lens, stream):
     return load_library().attn_fwd(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, key_lens, stream)
+
+
+def attn_fwd_varlen_bf16(q, k, v, o, lse, cu_seqlens, B, H, Hkv, total, max_seqlen, d, scale, causal, stream):
+    return load_library().attn_fwd_varlen_bf16(q, k, v, o, lse, cu_seqlens, B, H, Hkv, total, max_seqlen,
+                                               d, scale, causal, stream)
 
 
 def attn_bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, Hkv, N, d, scale, causal, key_lens, stream):
@@ -129,6 +136,47 @@ def forward(q, k, v, *, scale=None, causal=False, key_lens=None, out=None, lse=N
             key_lens.data_ptr() if key_lens is not None else None, stream)
     if st != ATTN_OK:
         raise AttnError(st, fn.__name__)
+    return out, lse
+
+
+def forward_varlen(q, k, v, cu_seqlens, max_seqlen, *, scale=None, causal=False, out=None, lse=None,
+                   stream=None):
+    """Forward pass over packed sequences (bf16 GPU tensors).
+
+    q: [total, H, d]; k, v: [total, Hkv, d]; cu_seqlens: int32 GPU tensor [B + 1]
+    of sequence offsets (0 = cu[0] <= cu[1] <= ... <= cu[B] = total); every
+    sequence length at most ``max_seqlen`` (an int: the device offsets are not
+    read on the host).  Returns (o, lse): o [total, H, d] bf16, lse fp32
+    [H, total].  Enqueued on ``stream`` (default: torch's current stream).
+    """
+    import torch
+
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, v must be 3-D: [total, H, d] and [total, Hkv, d]")
+    total, H, d = q.shape
+    Hkv = k.shape[1]
+    if tuple(k.shape) != (total, Hkv, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bfloat16 GPU tensor")
+    if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-D int32 GPU tensor [B + 1]")
+    cu_seqlens = cu_seqlens.contiguous()
+    B = cu_seqlens.numel() - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((H, total), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = attn_fwd_varlen_bf16(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                              cu_seqlens.data_ptr(), B, H, Hkv, total, int(max_seqlen), d, float(scale),
+                              int(bool(causal)), stream)
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_varlen_bf16")
     return out, lse
 
 

@@ -52,6 +52,8 @@ int validate(const void* q, const void* k, const void* v, const void* o, const v
     p->zero_q = !(c >= FLT_MIN);
     p->scale_log2 = p->zero_q ? 1.0f : c;
     p->negate_q = scale < 0.f;
+    p->cu_seqlens = nullptr;
+    p->total = 0;
     return ATTN_OK;
 }
 
@@ -141,6 +143,31 @@ int attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o, co
     bp.scale = scale;
     (void)hipGetLastError();
     const hipError_t e = attn::launch_bwd_bf16(bp, d, causal != 0, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int attn_fwd_varlen_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                         const int32_t* cu_seqlens, int B, int H, int Hkv, int total, int max_seqlen,
+                         int d, float scale, int causal, void* stream) {
+    if (total < 0) return ATTN_ERR_SHAPE;
+    attn::Params p;
+    bool empty = false;
+    // the generic checks, with the longest sequence in the role of N (and no
+    // sequence at all when there are no tokens)
+    const int st = validate(q, k, v, o, lse, total == 0 ? 0 : B, H, Hkv, max_seqlen, d, scale, causal, nullptr,
+                            &p, &empty);
+    if (st != ATTN_OK) return st;
+    // one sequence's query rows (tail tile included) are addressed with
+    // 32-bit byte offsets in the [total][H][d] layout
+    if ((int64_t)(max_seqlen + attn::kBR) * H * d * 2 >= ((int64_t)1 << 31)) return ATTN_ERR_SHAPE;
+    if (empty) return ATTN_OK;
+    if (!cu_seqlens) return ATTN_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) return ATTN_ERR_ALIGN;
+    p.cu_seqlens = cu_seqlens;
+    p.total = total;
+    (void)hipGetLastError();
+    const hipError_t e =
+        attn::launch_fwd_bf16(p, d, causal != 0, schedule_bf16(p, causal != 0), static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

@@ -33,6 +33,11 @@ struct Params {
     int negate_q;       // scale < 0: q is negated in registers and |scale| used
     int zero_q;         // scale == 0 (or |scale|·log2 e below the normal range):
                         // every score is 0, computed as q = 0 with c = 1
+    // Packed layout (bf16 forward only): device int32 [B + 1] sequence
+    // offsets into `total` token rows, N is then the longest sequence length;
+    // NULL for the [B][H][N][d] layout.
+    const int32_t* cu_seqlens;
+    int total;
 };
 
 // Backward pass: the forward's problem (q, k, v, lse, sizes, key_lens) plus
@@ -101,6 +106,56 @@ __device__ __forceinline__ int key_limit(const Params& p, int b, int q0, int* kv
     int lim = kv_len;
     if (CAUSAL) lim = min(lim, min(q0 + kBR, p.N));
     return lim;
+}
+
+// Where the rows of sequence b, query head h (kv head g) live.  [B][H][N][d]
+// layout: the N rows of one head are contiguous (stride d), the LSE is
+// [B][H][N] and key_lens cuts the keys.  Packed layout: sequence b holds
+// tokens cu_seqlens[b] .. cu_seqlens[b + 1] − 1 of [total][H][d] q / o and
+// [total][Hkv][d] k / v (the token-major, head-interleaved `b n (h d)`
+// activations of the aifi page's PyTorch example, with the sequences laid end
+// to end), so consecutive rows of one head are H·d (Hkv·d) elements apart, the
+// LSE is [H][total], and every token of the sequence is both a query and a
+// key.  Offsets are clamped into [0, total] and lengths to N on the device.
+struct Rows {
+    size_t q;       // element offset of query row 0 in q and o
+    size_t kv;      // element offset of key row 0 in k and v
+    size_t lse;     // index of query row 0 in lse
+    int q_stride;   // elements between consecutive query rows
+    int kv_stride;  // elements between consecutive key rows
+    int n_q;        // query rows
+    int kv_len;     // admissible keys (before any causal cut)
+};
+
+template <int D>
+__device__ __forceinline__ Rows rows_of(const Params& p, int b, int h, int g) {
+    Rows r;
+    if (p.cu_seqlens == nullptr) {
+        r.q = (size_t)(b * p.H + h) * p.N * D;
+        r.kv = (size_t)(b * p.Hkv + g) * p.N * D;
+        r.lse = (size_t)(b * p.H + h) * p.N;
+        r.q_stride = D;
+        r.kv_stride = D;
+        r.n_q = p.N;
+        int kv_len = p.N;
+        if (p.key_lens != nullptr) {
+            const int kl = p.key_lens[b];
+            kv_len = kl < 0 ? 0 : (kl > p.N ? p.N : kl);
+        }
+        r.kv_len = kv_len;
+    } else {
+        const int s0 = min(max(p.cu_seqlens[b], 0), p.total);
+        const int s1 = min(max(p.cu_seqlens[b + 1], s0), p.total);
+        const int len = min(s1 - s0, p.N);
+        r.q = ((size_t)s0 * p.H + h) * D;
+        r.kv = ((size_t)s0 * p.Hkv + g) * D;
+        r.lse = (size_t)h * p.total + s0;
+        r.q_stride = p.H * D;
+        r.kv_stride = p.Hkv * D;
+        r.n_q = len;
+        r.kv_len = len;
+    }
+    return r;
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }

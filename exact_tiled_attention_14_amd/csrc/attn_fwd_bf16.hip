@@ -113,20 +113,21 @@ struct Offsets {
     uint32_t k_rd;           // LDS: Sᵀ A operand, key block 0, d chunk 0
     uint32_t v_rd[G::DBLK];  // LDS (in the V tile): Oᵀ A operand of d block db, key block 0, c = 0, keys + 0..3
 
-    __device__ __forceinline__ void init(int wave, int lane) {
+    // row_bytes: distance in bytes between consecutive key rows in k and v
+    __device__ __forceinline__ void init(int wave, int lane, int row_bytes) {
         const int hl = lane >> 5, ql = lane & 31;
 #pragma unroll
         for (int i = 0; i < G::KI; ++i) {
             const int pos = 1024 * (wave + kWaves * i) + 16 * lane;  // LDS byte in the K tile
             const int row = pos / L::KROW, off = pos % L::KROW;
             // the 16 pad bytes of a row take a copy of the row's first chunk
-            k_src[i] = (uint32_t)(row * D * 2 + (off < D * 2 ? off : 0));
+            k_src[i] = (uint32_t)(row * row_bytes + (off < D * 2 ? off : 0));
         }
 #pragma unroll
         for (int i = 0; i < G::VI; ++i) {
             const int pos = 1024 * (wave + kWaves * i) + 16 * lane;  // LDS byte in the V tile
             const int key = pos / L::VROW;
-            v_src[i] = (uint32_t)(key * D * 2 + (L::vpos(key, pos % L::VROW) - key * L::VROW));
+            v_src[i] = (uint32_t)(key * row_bytes + (L::vpos(key, pos % L::VROW) - key * L::VROW));
         }
         k_rd = (uint32_t)(swap23(ql) * L::KROW + hl * 16);  // chunk 2c + hl is 32c bytes further
         // ds_read_b64_tr_b16: lane 16g + k addresses key 8(g / 2) + k / 4 at
@@ -140,18 +141,19 @@ struct Offsets {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// One K/V tile (keys kv0 .. kv0 + BC − 1 of the head) straight into an LDS
-// stage: each wave issues its share of the 1 KiB loads.  The descriptors
-// start at key kv0 and end at the key length, so rows past it are zeros:
-// NaN or any other content there can never reach the output.
+// One K/V tile (keys kv0 .. kv0 + BC − 1 of the head, rows `stride`
+// elements apart) straight into an LDS stage: each wave issues its share of
+// the 1 KiB loads.  The descriptors start at key kv0 and end at the key
+// length (or the tile's end), so rows past the key length are zeros: NaN or
+// any other content there can never reach the output.
 template <int D>
 __device__ __forceinline__ void load_tile(const Offsets<D>& o, char* stage, const uint16_t* kb,
-                                          const uint16_t* vb, int kv0, int kv_len, int wave) {
+                                          const uint16_t* vb, int kv0, int kv_len, int stride, int wave) {
 #if defined(__HIP_DEVICE_COMPILE__)  // (the LDS-destination builtin does not exist for the host pass)
     using G = Geo<D>;
-    const uint32_t bytes = (uint32_t)(kv_len - kv0) * (D * 2);
-    const __amdgpu_buffer_rsrc_t kres = make_rsrc(kb + (size_t)kv0 * D, bytes);
-    const __amdgpu_buffer_rsrc_t vres = make_rsrc(vb + (size_t)kv0 * D, bytes);
+    const uint32_t bytes = (uint32_t)min(kv_len - kv0, G::BC) * (uint32_t)(stride * 2);
+    const __amdgpu_buffer_rsrc_t kres = make_rsrc(kb + (size_t)kv0 * stride, bytes);
+    const __amdgpu_buffer_rsrc_t vres = make_rsrc(vb + (size_t)kv0 * stride, bytes);
 #pragma unroll
     for (int i = 0; i < G::KI; ++i) {
         const int t = wave + kWaves * i;
@@ -352,29 +354,35 @@ __device__ __forceinline__ void attend_tile(const Params& p, const Tile& t, cons
     const int qrow = q0w + ql;
     const int g = t.h / (p.H / p.Hkv);
 
-    int kv_len;
-    const int kv_hi = key_limit<CAUSAL>(p, t.b, q0, &kv_len);
+    const Rows R = rows_of<D>(p, t.b, t.h, g);
+    if (q0 >= R.n_q) return;  // (packed layout: past the end of a shorter sequence)
+    const int kv_len = R.kv_len;
+    // keys this workgroup looks at: the admissible ones, cut under a causal
+    // mask at the tile's last query row
+    const int kv_hi = CAUSAL ? min(kv_len, min(q0 + kBR, R.n_q)) : kv_len;
     const int ntiles = (kv_hi + BC - 1) / BC;
     const int niters = (ntiles + KSPLIT - 1) / KSPLIT;  // tile it = KSPLIT·j + grp
+    const int ks = R.kv_stride;
 
-    const uint16_t* qp = static_cast<const uint16_t*>(p.q) + ((size_t)(t.b * p.H + t.h) * p.N) * D;
-    const uint16_t* kb = static_cast<const uint16_t*>(p.k) + ((size_t)(t.b * p.Hkv + g) * p.N) * D;
-    const uint16_t* vb = static_cast<const uint16_t*>(p.v) + ((size_t)(t.b * p.Hkv + g) * p.N) * D;
+    const uint16_t* qp = static_cast<const uint16_t*>(p.q) + R.q;
+    const uint16_t* kb = static_cast<const uint16_t*>(p.k) + R.kv;
+    const uint16_t* vb = static_cast<const uint16_t*>(p.v) + R.kv;
 
     // Q rows of this lane as the Sᵀ B operand: chunk c holds d = 16c + 8h .. +7.
     // The sign flip / zeroing is applied after the first K/V tile's loads
     // are issued, so that nothing waits on the Q loads before those start.
     uint4 qu[G::DCH];
     {
-        const __amdgpu_buffer_rsrc_t qres = make_rsrc(qp, (uint32_t)p.N * (D * 2));
+        const __amdgpu_buffer_rsrc_t qres = make_rsrc(qp, (uint32_t)R.n_q * (uint32_t)(R.q_stride * 2));
 #pragma unroll
-        for (int c = 0; c < G::DCH; ++c) qu[c] = buf_load16(qres, (uint32_t)qrow * (D * 2) + c * 32 + hl * 16);
+        for (int c = 0; c < G::DCH; ++c)
+            qu[c] = buf_load16(qres, (uint32_t)qrow * (uint32_t)(R.q_stride * 2) + c * 32 + hl * 16);
     }
     uint32_t flip = p.negate_q ? 0x80008000u : 0u;
     uint32_t keep = p.zero_q ? 0u : 0xffffffffu;
 
     Offsets<D> o;
-    o.init(wave, lane);
+    o.init(wave, lane, ks * 2);
     // this group's two stages (in distinct LDS objects; see Lds)
     char* const S0 = lds.s0 + grp * G::STAGE;
     char* const S1 = lds.s1 + grp * G::STAGE;
@@ -390,7 +398,7 @@ __device__ __forceinline__ void attend_tile(const Params& p, const Tile& t, cons
         w.m_run = kNegInf;
         w.l_run = 0.f;
 
-        if (grp < ntiles) load_tile<D>(o, S0, kb, vb, grp * BC, kv_len, wave);
+        if (grp < ntiles) load_tile<D>(o, S0, kb, vb, grp * BC, kv_len, ks, wave);
         // (identity on the exact pass: flip and keep are reset below)
         bf16x8 qf[G::DCH];
 #pragma unroll
@@ -413,7 +421,7 @@ __device__ __forceinline__ void attend_tile(const Params& p, const Tile& t, cons
             constexpr int MODE = decltype(mode_tag)::value;
             const int it = KSPLIT * j + grp;
             const int kv0 = it * BC;
-            if (it + KSPLIT < ntiles) load_tile<D>(o, next, kb, vb, kv0 + KSPLIT * BC, kv_len, wave);
+            if (it + KSPLIT < ntiles) load_tile<D>(o, next, kb, vb, kv0 + KSPLIT * BC, kv_len, ks, wave);
             if (MODE == 1) {
                 tile<D, CAUSAL, 1>(w, cur, o, qf, c2, false, kv0, kv_len, qrow, hl, false);
             } else if (it < ntiles && !(CAUSAL && kv0 > q0w + 31)) {
@@ -497,8 +505,8 @@ __device__ __forceinline__ void attend_tile(const Params& p, const Tile& t, cons
     // ---- epilogue: O = Oᵀ/ℓ -> bf16, LSE
     const float l_tot = pair_sum(w.l_run);
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-    if (qrow < p.N) {
-        uint16_t* op = static_cast<uint16_t*>(p.o) + ((size_t)(t.b * p.H + t.h) * p.N + qrow) * D;
+    if (qrow < R.n_q) {
+        uint16_t* op = static_cast<uint16_t*>(p.o) + R.q + (size_t)qrow * R.q_stride;
 #pragma unroll
         for (int db = 0; db < G::DBLK; ++db)
 #pragma unroll
@@ -510,7 +518,7 @@ __device__ __forceinline__ void attend_tile(const Params& p, const Tile& t, cons
             }
         if (hl == 0) {
             const float lse = l_tot > 0.f ? (w.m_run + log2f(l_tot)) * kLn2 : kNegInf;
-            p.lse[(size_t)(t.b * p.H + t.h) * p.N + qrow] = lse;
+            p.lse[R.lse + qrow] = lse;
         }
     }
 }

@@ -69,6 +69,29 @@ int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float
                  int B, int H, int Hkv, int N, int d, float scale, int causal,
                  const int32_t* key_lens, void* stream);
 
+/* Packed variable-length sequences, bf16 (the padding handling of the aifi
+ * page, production tips, dynamic sequences: padded positions must not take
+ * part; here the sequences are packed end to end so that no padding exists).
+ * Sequence b (0 <= b < B) is tokens s_b .. e_b − 1 with s_b = cu_seqlens[b],
+ * e_b = cu_seqlens[b + 1]; within it the operation above applies with
+ * N = key_len = e_b − s_b and query row i = token s_b + i:
+ *     q, o : [total][H][d]     k, v : [total][Hkv][d]     lse : [H][total] fp32
+ * (token-major, heads interleaved: the `b n (h d)` activations of the aifi
+ * page's PyTorch example with the sequences laid end to end).  Every token of
+ * a sequence is a query and a key of that sequence only; causal == 1 admits
+ * keys j <= i of the same sequence.  cu_seqlens is int32 [B + 1] in DEVICE
+ * memory (4-byte aligned) and must satisfy 0 = cu[0] <= cu[1] <= ... <=
+ * cu[B] = total and e_b − s_b <= max_seqlen; the device clamps offsets into
+ * [0, total] and lengths to max_seqlen, so bad offsets cannot make it read or
+ * write out of bounds, but tokens they leave out are not written.  Sizes:
+ * B >= 0, total >= 0, max_seqlen >= 0 (B, total or max_seqlen == 0: no-op),
+ * the limits of attn_fwd_bf16 with N = max_seqlen, and (max_seqlen + 128)·H·d·2
+ * below 2^31.  Same status codes and check order as attn_fwd_bf16; the other
+ * pointers must be 16-byte aligned.  Enqueued on `stream`, not waited on. */
+int attn_fwd_varlen_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                         const int32_t* cu_seqlens, int B, int H, int Hkv, int total, int max_seqlen,
+                         int d, float scale, int causal, void* stream);
+
 /* Backward pass, bf16 (gradients of L = Σ O ∘ dout through the operation
  * above; the attention weights are recomputed from q, k and the forward's lse
  * rather than stored: unite.ai page "闪电注意力：革命性地提高Transformer效率",

@@ -11,7 +11,9 @@ Every function here is pinned by a ``-m "not gpu"`` test in ``tests/`` against
 something other than itself (closed forms, invariants, a library routine,
 brute force over every block size); see ``tests/test_oracle_pins.py`` and
 ``tests/test_oracle_blockwise.py``; the backward pass against torch autograd,
-finite differences and invariants in ``tests/test_oracle_backward.py``.  No
+finite differences and invariants in ``tests/test_oracle_backward.py``; the
+packed-sequence form against brute force and invariants in
+``tests/test_oracle_varlen.py``.  No
 function here is "parity unpinned".
 """
 
@@ -19,6 +21,7 @@ from .attention import (  # noqa: F401
     admissible,
     attention,
     attention_backward,
+    attention_varlen,
     blockwise_attention,
     kv_head_of,
     merge_partials,

@@ -18,6 +18,8 @@ Sources (web pages on exact tiled attention):
 * aifi multi-head attention page (qqiyuan.cn), section "动态序列处理": padded
   positions are ignored through an attention mask.
 * same unite.ai page, section "闪电注意力-2": grouped-query attention.
+* aifi page, PyTorch example: activations stored token-major with the heads
+  side by side (``b n (h d)``), the layout of the packed-sequence oracle.
 
 Readings where the pages are silent (each listed in the design doc):
 causal admits keys j ≤ i; key padding admits j < key_len_b; grouped query
@@ -39,6 +41,7 @@ __all__ = [
     "merge_partials",
     "merge_softmax",
     "attention_backward",
+    "attention_varlen",
 ]
 
 
@@ -262,3 +265,39 @@ def attention_backward(q, k, v, dout, scale, causal=False, key_lens=None):
             dq[b, h] = scale * (ds @ kv_k)
             dk[b, g, :kl] += scale * (ds.T @ q[b, h])
     return dq, dk, dv
+
+
+def attention_varlen(q, k, v, cu_seqlens, scale, causal=False):
+    """Exact attention over packed sequences.
+
+    The sequences of a batch are laid end to end along the token axis of
+    q [total, H, d] and k, v [total, Hkv, d] (the token-major ``b n (h d)``
+    activations of the aifi page's PyTorch example, one sequence after the
+    other), so padding never exists (aifi page, section "动态序列处理": padded
+    positions must take no part).  Sequence b is tokens cu_seqlens[b] ..
+    cu_seqlens[b + 1] − 1; it is the standard attention problem on its own
+    tokens (query row i = its i-th token, keys = its tokens, causal keeps
+    j ≤ i within the sequence), solved by ``attention`` with B = 1.
+
+    Returns (O, LSE): O fp64 [total, H, d], LSE fp64 [H, total].
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    total, H, d = q.shape
+    Hkv = k.shape[1]
+    cu = [int(x) for x in cu_seqlens]
+    assert k.shape == (total, Hkv, d) and v.shape == k.shape
+    assert cu[0] == 0 and cu[-1] == total and all(a <= b for a, b in zip(cu, cu[1:]))
+    O = np.zeros((total, H, d))
+    LSE = np.full((H, total), -np.inf)
+    for b in range(len(cu) - 1):
+        s0, s1 = cu[b], cu[b + 1]
+        if s1 == s0:
+            continue
+        # [len, heads, d] -> [1, heads, len, d]
+        qs = q[s0:s1].transpose(1, 0, 2)[None]
+        ks = k[s0:s1].transpose(1, 0, 2)[None]
+        vs = v[s0:s1].transpose(1, 0, 2)[None]
+        o_b, lse_b = attention(qs, ks, vs, scale, causal=causal)
+        O[s0:s1] = o_b[0].transpose(1, 0, 2)
+        LSE[:, s0:s1] = lse_b[0]
+    return O, LSE

@@ -137,3 +137,49 @@ def call_bwd(**over):
 ])
 def test_backward_host_validation(over, status):
     assert call_bwd(**over) == status
+
+
+VAR_GOOD = dict(q=P, k=P * 2, v=P * 3, o=P * 4, lse=P * 5, cu=P * 6, B=3, H=4, Hkv=2, total=300,
+                max_seqlen=200, d=128, scale=0.125, causal=1, stream=None)
+
+
+def call_varlen(**over):
+    a = dict(VAR_GOOD, **over)
+    return attn.attn_fwd_varlen_bf16(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cu"], a["B"], a["H"], a["Hkv"],
+                                     a["total"], a["max_seqlen"], a["d"], a["scale"], a["causal"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(d=96), attn.ATTN_ERR_HEAD_DIM),
+    (dict(H=3, Hkv=2), attn.ATTN_ERR_SHAPE),
+    (dict(B=-1), attn.ATTN_ERR_SHAPE),
+    (dict(total=-1), attn.ATTN_ERR_SHAPE),
+    (dict(max_seqlen=-1), attn.ATTN_ERR_SHAPE),
+    (dict(causal=2), attn.ATTN_ERR_SHAPE),
+    # one sequence's query rows must be addressable with 32-bit byte offsets
+    (dict(H=64, Hkv=64, max_seqlen=2**17 - 128), attn.ATTN_ERR_SHAPE),
+    (dict(scale=math.nan), attn.ATTN_ERR_SCALE),
+    (dict(q=None), attn.ATTN_ERR_NULL),
+    (dict(lse=None), attn.ATTN_ERR_NULL),
+    (dict(cu=None), attn.ATTN_ERR_NULL),
+    (dict(k=P + 8), attn.ATTN_ERR_ALIGN),
+    (dict(cu=P + 2), attn.ATTN_ERR_ALIGN),
+    # int32 offsets only need their natural alignment
+    (dict(B=0, cu=P + 4, q=None, k=None, v=None, o=None, lse=None), attn.ATTN_OK),
+    # empty problems are a no-op and may pass NULL pointers
+    (dict(B=0, q=None, k=None, v=None, o=None, lse=None, cu=None), attn.ATTN_OK),
+    (dict(total=0, q=None, k=None, v=None, o=None, lse=None, cu=None), attn.ATTN_OK),
+    (dict(max_seqlen=0, q=None, k=None, v=None, o=None, lse=None, cu=None), attn.ATTN_OK),
+])
+def test_varlen_host_validation(over, status):
+    assert call_varlen(**over) == status
+
+
+def test_python_forward_varlen_rejects_bad_tensors():
+    import torch
+    q = torch.zeros(8, 2, 64, dtype=torch.bfloat16)
+    cu = torch.tensor([0, 8], dtype=torch.int32)
+    with pytest.raises(ValueError):
+        attn.forward_varlen(q, q, q, cu, 8)              # CPU tensors
+    with pytest.raises(ValueError):
+        attn.forward_varlen(q[None], q, q, cu, 8)        # wrong rank

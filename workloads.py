@@ -75,6 +75,33 @@ def make_inputs(w: Workload):
     return make_qkv(w.B, w.H, w.Hkv, w.N, w.d, w.dtype, w.seed, w.padded)
 
 
+# Packed variable-length batch (the aifi page's dynamic-sequence case, with
+# the key-length mix of the padded workload: lengths uniform on N/2 .. N):
+# sequences laid end to end, token-major [total, H, d], causal.
+VARLEN = dict(name="packed varlen B8 lengths U[4096,8192] Hq32 Hkv8 d128 causal bf16",
+              B=8, N=8192, H=32, Hkv=8, d=128, causal=True, seed=6)
+
+
+def varlen_lengths(B, lo, hi, seed):
+    """B sequence lengths drawn uniformly from the integers lo .. hi inclusive
+    (a torch.Generator('cpu') seeded with ``seed``)."""
+    g = torch.Generator("cpu").manual_seed(int(seed))
+    return torch.randint(lo, hi + 1, (B,), generator=g, dtype=torch.int64).tolist()
+
+
+def make_varlen(lengths, H, Hkv, d, seed=0):
+    """Packed bf16 inputs for the given sequence lengths, following the recipe
+    above (Q, K, V drawn in that order as N(0, 1) float32, rounded to bf16):
+    q [total, H, d], k and v [total, Hkv, d], and cu_seqlens int32 [B + 1]."""
+    total = int(sum(lengths))
+    g = torch.Generator("cpu").manual_seed(int(seed))
+    q = torch.randn((total, H, d), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    k = torch.randn((total, Hkv, d), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    v = torch.randn((total, Hkv, d), generator=g, dtype=torch.float32).to(torch.bfloat16)
+    cu = torch.tensor([0] + list(np.cumsum(lengths, dtype=np.int64)), dtype=torch.int32)
+    return q, k, v, cu
+
+
 def as_f64(t):
     """Exact fp64 numpy copy of a CPU tensor (bf16 and fp32 both embed exactly)."""
     return t.detach().to("cpu", torch.float64).numpy()
