@@ -181,6 +181,42 @@ class VarlenRunner(Runner):
         return 4.0 * s["d"] * s["H"] * pairs
 
 
+class SplitKVRunner(Runner):
+    """The split-KV shape (attn_fwd_splitkv_bf16) resident on the GPU, with
+    its workspace; ``launch_one`` times the same problem as one key range."""
+
+    def __init__(self, spec, dev, splits=None):
+        import torch
+
+        import exact_tiled_attention_14_amd as attn
+
+        self.spec = spec
+        s = spec
+        g = torch.Generator("cpu").manual_seed(s["seed"])
+        q = torch.randn((s["B"], s["H"], s["Nq"], s["d"]), generator=g).to(torch.bfloat16)
+        k = torch.randn((s["B"], s["Hkv"], s["Nk"], s["d"]), generator=g).to(torch.bfloat16)
+        v = torch.randn((s["B"], s["Hkv"], s["Nk"], s["d"]), generator=g).to(torch.bfloat16)
+        self.q, self.k, self.v = q.to(dev), k.to(dev), v.to(dev)
+        self.o = torch.empty_like(self.q)
+        self.lse = torch.empty((s["B"], s["H"], s["Nq"]), dtype=torch.float32, device=dev)
+        self.splits = s["splits"] if splits is None else splits
+        self.nbytes = attn.attn_splitkv_workspace_bytes(s["B"], s["H"], s["Nq"], s["d"], self.splits)
+        self.ws = torch.empty(max(self.nbytes, 16), dtype=torch.uint8, device=dev)
+        self.stream = torch.cuda.current_stream(dev)
+        self.fn = attn.attn_fwd_splitkv_bf16
+        scale = float(1.0 / math.sqrt(s["d"]))
+        self.args = (self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), self.o.data_ptr(),
+                     self.lse.data_ptr(), s["B"], s["H"], s["Hkv"], s["Nq"], s["Nk"], s["d"], scale,
+                     int(s["causal"]), s["Nk"] - s["Nq"], 0, None, self.splits, self.ws.data_ptr(), self.nbytes,
+                     self.stream.cuda_stream)
+
+    def algorithmic_flops(self):
+        s = self.spec
+        nq, nk = s["Nq"], s["Nk"]
+        pairs = nq * (nk - nq) + nq * (nq + 1) / 2 if s["causal"] else nq * nk
+        return 4.0 * s["d"] * s["H"] * s["B"] * pairs
+
+
 def cpu_baseline(w, budget_s=10.0):
     """The fp64 oracle, as it stands, on this host's cores over a bounded sample
     of the workload: whole (b, h) heads, all query rows, in order, repeating
@@ -234,6 +270,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip timing the other bf16 workloads")
     ap.add_argument("--no-backward", action="store_true", help="skip timing the backward pass")
     ap.add_argument("--no-varlen", action="store_true", help="skip timing the packed variable-length batch")
+    ap.add_argument("--no-splitkv", action="store_true", help="skip timing the split-KV shape")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 3 device-to-device copies of MIB MiB (a plain copy kernel of known "
                          "traffic, to calibrate the FETCH_SIZE / WRITE_SIZE counters)")
@@ -343,6 +380,21 @@ def main():
                           "algorithmic_tflops": round(a / (m * 1e-3) / 1e12, 2),
                           "frac_of_bf16_peak": round(a / (m * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
         del vr
+
+    if not args.no_splitkv:
+        from workloads import SPLITKV
+
+        res = {"workload": SPLITKV["name"]}
+        for splits in (1, SPLITKV["splits"]):
+            sr = SplitKVRunner(SPLITKV, dev, splits=splits)
+            steps = max(10, min(args.steps, 50))
+            m = sr.time(steps, 3)
+            a = sr.algorithmic_flops()
+            res["one_range" if splits == 1 else f"{splits}_ranges"] = {
+                "ms": round(m, 4), "steps": steps, "algorithmic_tflops": round(a / (m * 1e-3) / 1e12, 2),
+                "frac_of_bf16_peak": round(a / (m * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+            del sr
+        line["splitkv"] = res
 
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)

@@ -2,10 +2,12 @@
 
 Thin ctypes layer over ``libattn.so`` (see ``include/attn.h``): the functions
 ``attn_fwd_bf16``, ``attn_fwd_f32``, ``attn_fwd``, ``attn_fwd_varlen_bf16``,
-``attn_bwd_bf16`` and ``attn_status_str`` take the same arguments as the C
-entry points (device pointers as Python ints) and return the status code.
-``forward``, ``forward_varlen`` and ``backward`` marshal torch tensors onto
-them; every step of the computation
+``attn_fwd_partial_bf16``, ``attn_merge``, ``attn_fwd_splitkv_bf16``,
+``attn_splitkv_workspace_bytes``, ``attn_bwd_bf16`` and ``attn_status_str``
+take the same arguments as the C entry points (device pointers as Python
+ints) and return what they return.  ``forward``, ``forward_varlen``,
+``forward_partial``, ``merge``, ``forward_splitkv`` and ``backward`` marshal
+torch tensors onto them; every step of the computation
 runs in the HIP kernels.  There is no fallback: if the library is missing,
 every call raises.
 """
@@ -16,13 +18,16 @@ import os
 
 __all__ = [
     "AttnError", "attn_fwd", "attn_fwd_bf16", "attn_fwd_f32", "attn_fwd_varlen_bf16", "attn_bwd_bf16",
-    "attn_status_str", "forward", "forward_varlen", "backward", "library_path", "load_library",
+    "attn_fwd_partial_bf16", "attn_merge", "attn_fwd_splitkv_bf16", "attn_splitkv_workspace_bytes",
+    "attn_status_str", "forward", "forward_varlen", "forward_partial", "merge", "forward_splitkv", "backward",
+    "library_path", "load_library", "ATTN_ERR_WORKSPACE", "ATTN_MAX_SPLITS",
     "ATTN_OK", "ATTN_ERR_NULL", "ATTN_ERR_SHAPE", "ATTN_ERR_HEAD_DIM", "ATTN_ERR_ALIGN",
     "ATTN_ERR_SCALE", "ATTN_ERR_HIP",
 ]
 
 ATTN_OK, ATTN_ERR_NULL, ATTN_ERR_SHAPE, ATTN_ERR_HEAD_DIM = 0, 1, 2, 3
-ATTN_ERR_ALIGN, ATTN_ERR_SCALE, ATTN_ERR_HIP = 4, 5, 6
+ATTN_ERR_ALIGN, ATTN_ERR_SCALE, ATTN_ERR_HIP, ATTN_ERR_WORKSPACE = 4, 5, 6, 7
+ATTN_MAX_SPLITS = 64
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -36,6 +41,11 @@ ENTRY_POINTS = {
     "attn_fwd_f32": (_FWD_ARGS, ctypes.c_int),
     "attn_fwd": (_FWD_ARGS, ctypes.c_int),
     "attn_fwd_varlen_bf16": ([_P] * 6 + [_I] * 6 + [ctypes.c_float, _I, _P], ctypes.c_int),
+    "attn_fwd_partial_bf16": ([_P] * 5 + [_I] * 6 + [ctypes.c_float, _I, _I, _I, _P], ctypes.c_int),
+    "attn_merge": ([_P, _P] + [_I] * 5 + [_P, _I, _P, _P], ctypes.c_int),
+    "attn_fwd_splitkv_bf16": ([_P] * 5 + [_I] * 6 + [ctypes.c_float, _I, _I, _I, _P, _I, _P, ctypes.c_size_t, _P],
+                              ctypes.c_int),
+    "attn_splitkv_workspace_bytes": ([_I] * 5, ctypes.c_size_t),
     "attn_bwd_bf16": ([_P] * 10 + [_I, _I, _I, _I, _I, ctypes.c_float, _I, _P, _P], ctypes.c_int),
     "attn_status_str": ([_I], ctypes.c_char_p),
 }
@@ -86,6 +96,26 @@ def attn_fwd(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, key_lens, stream):
 def attn_fwd_varlen_bf16(q, k, v, o, lse, cu_seqlens, B, H, Hkv, total, max_seqlen, d, scale, causal, stream):
     return load_library().attn_fwd_varlen_bf16(q, k, v, o, lse, cu_seqlens, B, H, Hkv, total, max_seqlen,
                                                d, scale, causal, stream)
+
+
+def attn_fwd_partial_bf16(q, k, v, o_part, lse_part, B, H, Hkv, Nq, Nk, d, scale, causal, q_offset, k_offset,
+                          stream):
+    return load_library().attn_fwd_partial_bf16(q, k, v, o_part, lse_part, B, H, Hkv, Nq, Nk, d, scale, causal,
+                                                q_offset, k_offset, stream)
+
+
+def attn_merge(o_parts, lse_parts, S, B, H, N, d, o, o_bf16, lse, stream):
+    return load_library().attn_merge(o_parts, lse_parts, S, B, H, N, d, o, o_bf16, lse, stream)
+
+
+def attn_fwd_splitkv_bf16(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, q_offset, k_offset, key_lens,
+                          num_splits, workspace, workspace_bytes, stream):
+    return load_library().attn_fwd_splitkv_bf16(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, q_offset,
+                                                k_offset, key_lens, num_splits, workspace, workspace_bytes, stream)
+
+
+def attn_splitkv_workspace_bytes(B, H, N, d, num_splits):
+    return load_library().attn_splitkv_workspace_bytes(B, H, N, d, num_splits)
 
 
 def attn_bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, Hkv, N, d, scale, causal, key_lens, stream):
@@ -178,6 +208,102 @@ def forward_varlen(q, k, v, cu_seqlens, max_seqlen, *, scale=None, causal=False,
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd_varlen_bf16")
     return out, lse
+
+
+def _check_bf16(**tensors):
+    import torch
+
+    for name, t in tensors.items():
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bfloat16 GPU tensor")
+
+
+def forward_partial(q, k, v, *, q_offset=0, k_offset=0, scale=None, causal=False, stream=None):
+    """Attention of q [B, H, Nq, d] over one key block k, v [B, Hkv, Nk, d]
+    (bf16 GPU tensors) whose first query / key sit at positions q_offset /
+    k_offset.  Returns (o_part fp32 [B, H, Nq, d], lse_part fp32 [B, H, Nq])."""
+    import torch
+
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D")
+    B, H, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, Hkv, Nk, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("shape mismatch")
+    _check_bf16(q=q, k=k, v=v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty((B, H, Nq, d), dtype=torch.float32, device=q.device)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = attn_fwd_partial_bf16(q.data_ptr(), k.data_ptr() if Nk else None, v.data_ptr() if Nk else None,
+                               o.data_ptr(), lse.data_ptr(), B, H, Hkv, Nq, Nk, d, float(scale), int(bool(causal)),
+                               int(q_offset), int(k_offset), stream)
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_partial_bf16")
+    return o, lse
+
+
+def merge(o_parts, lse_parts, *, out_dtype=None, stream=None):
+    """Combine partials o_parts fp32 [S, B, H, N, d], lse_parts fp32
+    [S, B, H, N] into (o [B, H, N, d] of out_dtype (bf16 default), lse fp32)."""
+    import torch
+
+    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out_dtype must be bfloat16 or float32")
+    S, B, H, N, d = o_parts.shape
+    for name, t in (("o_parts", o_parts), ("lse_parts", lse_parts)):
+        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 GPU tensor")
+    if tuple(lse_parts.shape) != (S, B, H, N):
+        raise ValueError("lse_parts shape mismatch")
+    o = torch.empty((B, H, N, d), dtype=out_dtype, device=o_parts.device)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=o_parts.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(o_parts.device).cuda_stream
+    st = attn_merge(o_parts.data_ptr(), lse_parts.data_ptr(), S, B, H, N, d, o.data_ptr(),
+                    int(out_dtype == torch.bfloat16), lse.data_ptr(), stream)
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_merge")
+    return o, lse
+
+
+def forward_splitkv(q, k, v, num_splits, *, q_offset=0, k_offset=0, scale=None, causal=False, key_lens=None):
+    """Attention of q [B, H, Nq, d] over k, v [B, Hkv, Nk, d] (bf16 GPU
+    tensors; positions as in forward_partial) computed over ``num_splits``
+    key ranges and merged.  Returns (o bf16 [B, H, Nq, d], lse fp32
+    [B, H, Nq]).  The workspace is a torch allocation released when this
+    returns; the launches go to torch's current stream, which orders them
+    before any later reuse of that memory."""
+    import torch
+
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D")
+    B, H, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, Hkv, Nk, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("shape mismatch")
+    _check_bf16(q=q, k=k, v=v)
+    if key_lens is not None:
+        if key_lens.dtype != torch.int32 or not key_lens.is_cuda or key_lens.numel() != B:
+            raise ValueError("key_lens must be an int32 GPU tensor with B entries")
+        key_lens = key_lens.contiguous()
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    nbytes = attn_splitkv_workspace_bytes(B, H, Nq, d, int(num_splits))
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = attn_fwd_splitkv_bf16(q.data_ptr(), k.data_ptr() if Nk else None, v.data_ptr() if Nk else None,
+                               o.data_ptr(), lse.data_ptr(), B, H, Hkv, Nq, Nk, d, float(scale), int(bool(causal)),
+                               int(q_offset), int(k_offset), key_lens.data_ptr() if key_lens is not None else None,
+                               int(num_splits), ws.data_ptr(), nbytes, stream)
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_splitkv_bf16")
+    return o, lse
 
 
 def backward(q, k, v, o, lse, dout, *, scale=None, causal=False, key_lens=None, stream=None):

@@ -11,6 +11,8 @@ namespace attn {
 hipError_t launch_fwd_bf16(const Params& p, int d, bool causal, const Schedule& sc, hipStream_t stream);
 hipError_t launch_fwd_f32(const Params& p, int d, bool causal, hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool causal, hipStream_t stream);
+hipError_t launch_merge(const float* o_parts, const float* lse_parts, int S, int64_t rows, int d, void* o,
+                        bool o_bf16, float* lse, hipStream_t stream);
 }  // namespace attn
 
 namespace {
@@ -54,6 +56,11 @@ int validate(const void* q, const void* k, const void* v, const void* o, const v
     p->negate_q = scale < 0.f;
     p->cu_seqlens = nullptr;
     p->total = 0;
+    p->Nk = N;
+    p->splits = 1;
+    p->chunk = N;
+    p->delta = 0;
+    p->o_f32 = nullptr;
     return ATTN_OK;
 }
 
@@ -79,7 +86,7 @@ int device_cus() {
 // grid has fewer than two workgroups per CU.  (At d = 64 one workgroup needs
 // few enough registers and LDS for three per CU when the grid is large.)
 attn::Schedule schedule_bf16(const attn::Params& p, bool causal) {
-    const int64_t items = (int64_t)p.B * p.H * p.q_tiles;
+    const int64_t items = (int64_t)p.B * p.H * p.q_tiles * p.splits;
     const int cus = device_cus();
     attn::Schedule sc;
     if (causal && items < 4 * (int64_t)cus) {
@@ -171,6 +178,106 @@ int attn_fwd_varlen_bf16(const void* q, const void* k, const void* v, void* o, f
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
+int attn_fwd_partial_bf16(const void* q, const void* k, const void* v, float* o_part, float* lse_part,
+                          int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                          int q_offset, int k_offset, void* stream) {
+    if (Nk < 0 || (int64_t)Nk * d * 4 >= ((int64_t)1 << 31)) return ATTN_ERR_SHAPE;
+    attn::Params p;
+    bool empty = false;
+    // the generic checks with the query rows in the role of N (a key block
+    // with no keys may come with NULL k and v: nothing is read from them)
+    const void* kk = Nk == 0 ? q : k;
+    const void* vv = Nk == 0 ? q : v;
+    const int st = validate(q, kk, vv, o_part, lse_part, B, H, Hkv, Nq, d, scale, causal, nullptr, &p, &empty);
+    if (st != ATTN_OK || empty) return st;
+    p.k = kk;
+    p.v = vv;
+    p.Nk = Nk;
+    p.chunk = Nk;
+    // key j admissible for row i iff k_offset + j <= q_offset + i; clamped
+    // to the range where it still decides something
+    const int64_t delta = (int64_t)q_offset - k_offset;
+    p.delta = (int)(delta < -(int64_t)Nq - 1 ? -(int64_t)Nq - 1 : (delta > (int64_t)Nk + 1 ? (int64_t)Nk + 1 : delta));
+    p.o = nullptr;
+    p.o_f32 = o_part;
+    (void)hipGetLastError();
+    const hipError_t e =
+        attn::launch_fwd_bf16(p, d, causal != 0, schedule_bf16(p, causal != 0), static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int attn_merge(const float* o_parts, const float* lse_parts, int S, int B, int H, int N, int d,
+               void* o, int o_bf16, float* lse, void* stream) {
+    if (S < 1 || B < 0 || H < 1 || N < 0 || (o_bf16 != 0 && o_bf16 != 1)) return ATTN_ERR_SHAPE;
+    if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
+    if ((int64_t)S * B * H * N > ((int64_t)1 << 62) / (d + 1)) return ATTN_ERR_SHAPE;
+    if ((int64_t)B * H * N * (d / 4) / 256 >= ((int64_t)1 << 31)) return ATTN_ERR_SHAPE;
+    if (B == 0 || N == 0) return ATTN_OK;
+    if (!o_parts || !lse_parts || !o || !lse) return ATTN_ERR_NULL;
+    if (!aligned16(o_parts) || !aligned16(lse_parts) || !aligned16(o) || !aligned16(lse)) return ATTN_ERR_ALIGN;
+    (void)hipGetLastError();
+    const hipError_t e = attn::launch_merge(o_parts, lse_parts, S, (int64_t)B * H * N, d, o, o_bf16 != 0, lse,
+                                            static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+namespace {
+// keys per split: ceil(N / S) rounded up to whole 128-key tiles
+int split_chunk(int N, int S) {
+    const int64_t c = ((int64_t)N + S - 1) / S;
+    return (int)((c + 127) / 128 * 128);
+}
+}  // namespace
+
+size_t attn_splitkv_workspace_bytes(int B, int H, int N, int d, int num_splits) {
+    if (B < 0 || H < 1 || N < 0 || (d != 64 && d != 128) || num_splits < 1 || num_splits > ATTN_MAX_SPLITS) return 0;
+    return (size_t)num_splits * B * H * N * (d + 1) * sizeof(float);
+}
+
+int attn_fwd_splitkv_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                          int q_offset, int k_offset, const int32_t* key_lens, int num_splits,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    if (Nk < 0 || (int64_t)Nk * d * 4 >= ((int64_t)1 << 31)) return ATTN_ERR_SHAPE;
+    attn::Params p;
+    bool empty = false;
+    const void* kk = Nk == 0 ? q : k;
+    const void* vv = Nk == 0 ? q : v;
+    const int st = validate(q, kk, vv, o, lse, B, H, Hkv, Nq, d, scale, causal, key_lens, &p, &empty);
+    if (st != ATTN_OK) return st;
+    if (num_splits < 1 || num_splits > ATTN_MAX_SPLITS) return ATTN_ERR_SHAPE;
+    if ((int64_t)B * H * p.q_tiles * num_splits > kMaxWorkgroups) return ATTN_ERR_SHAPE;
+    if (empty) return ATTN_OK;
+    p.k = kk;
+    p.v = vv;
+    p.Nk = Nk;
+    p.chunk = Nk;
+    const int64_t delta = (int64_t)q_offset - k_offset;
+    p.delta = (int)(delta < -(int64_t)Nq - 1 ? -(int64_t)Nq - 1 : (delta > (int64_t)Nk + 1 ? (int64_t)Nk + 1 : delta));
+    const int chunk = split_chunk(Nk, num_splits);
+    const int S = Nk == 0 ? 1 : (Nk + chunk - 1) / chunk;  // ranges actually used (at most num_splits)
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    if (S == 1) {  // one range: the plain forward pass
+        const hipError_t e = attn::launch_fwd_bf16(p, d, causal != 0, schedule_bf16(p, causal != 0), hs);
+        return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+    }
+    const size_t need = attn_splitkv_workspace_bytes(B, H, Nq, d, num_splits);
+    if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
+    float* o_parts = static_cast<float*>(workspace);
+    float* lse_parts = o_parts + (size_t)S * B * H * Nq * d;
+    p.o = nullptr;
+    p.splits = S;
+    p.chunk = chunk;
+    p.o_f32 = o_parts;
+    p.lse = lse_parts;
+    hipError_t e = attn::launch_fwd_bf16(p, d, causal != 0, schedule_bf16(p, causal != 0), hs);
+    if (e != hipSuccess) return ATTN_ERR_HIP;
+    e = attn::launch_merge(o_parts, lse_parts, S, (int64_t)B * H * Nq, d, o, true, lse, hs);
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int H, int Hkv, int N, int d, float scale, int causal,
              const int32_t* key_lens, void* stream) {
@@ -186,6 +293,7 @@ const char* attn_status_str(int status) {
         case ATTN_ERR_ALIGN: return "a pointer is not 16-byte aligned";
         case ATTN_ERR_SCALE: return "scale must be finite";
         case ATTN_ERR_HIP: return "HIP kernel launch failed";
+        case ATTN_ERR_WORKSPACE: return "workspace missing or smaller than attn_splitkv_workspace_bytes";
         default: return "unknown attn status";
     }
 }

@@ -38,6 +38,19 @@ struct Params {
     // NULL for the [B][H][N][d] layout.
     const int32_t* cu_seqlens;
     int total;
+    // Key range and output of the bf16 forward.  Nk: rows per kv head in k
+    // and v ([B][Hkv][Nk][d]; N unless the keys are a block of their own).
+    // splits > 1: the launch covers `splits` consecutive key ranges of `chunk`
+    // keys each (the last one shorter), one partial result per range.
+    // delta: under a causal mask key j of the range is admissible for query
+    // row i iff j <= i + delta (0 when queries and keys start together).
+    // o_f32 non-NULL: O goes there in fp32, [splits][B][H][N][d], with lse as
+    // [splits][B][H][N], instead of bf16 into o.
+    int Nk;
+    int splits;
+    int chunk;
+    int delta;
+    float* o_f32;
 };
 
 // Backward pass: the forward's problem (q, k, v, lse, sizes, key_lens) plus
@@ -72,20 +85,28 @@ struct Schedule {
 // FlashAttention-2 improvements listed in the FlashAttention2 code block of
 // the zsdodo.com page).
 struct Tile {
-    int b, h, tile;
+    int b, h, tile, split;
 };
 
-template <bool CAUSAL>
+// GEN: the launch may carry several key splits (the plain kernels never do,
+// and skip the arithmetic for them).
+template <bool CAUSAL, bool GEN = false>
 __device__ __forceinline__ Tile map_workgroup(const Params& p) {
     const int G = gridDim.x;
     const int w = blockIdx.x;
     const int x = w % kXcds, k = w / kXcds;
     const int per = G / kXcds, extra = G % kXcds;
     const int logical = x * per + min(x, extra) + k;
-    const int hb = logical / p.q_tiles;
-    int t = logical - hb * p.q_tiles;
+    const int shb = logical / p.q_tiles;  // (split, h, b), b fastest
+    int t = logical - shb * p.q_tiles;
     if (CAUSAL) t = p.q_tiles - 1 - t;
     Tile r;
+    r.split = 0;
+    int hb = shb;
+    if (GEN && p.splits > 1) {
+        r.split = shb / (p.H * p.B);
+        hb = shb - r.split * (p.H * p.B);
+    }
     r.h = hb / p.B;
     r.b = hb - r.h * p.B;
     r.tile = t;
@@ -118,42 +139,67 @@ __device__ __forceinline__ int key_limit(const Params& p, int b, int q0, int* kv
 // LSE is [H][total], and every token of the sequence is both a query and a
 // key.  Offsets are clamped into [0, total] and lengths to N on the device.
 struct Rows {
-    size_t q;       // element offset of query row 0 in q and o
-    size_t kv;      // element offset of key row 0 in k and v
+    size_t q;       // element offset of query row 0 in q
+    size_t o;       // element offset of query row 0 in the output (o or o_f32)
+    size_t kv;      // element offset of key row 0 of the range in k and v
     size_t lse;     // index of query row 0 in lse
     int q_stride;   // elements between consecutive query rows
     int kv_stride;  // elements between consecutive key rows
     int n_q;        // query rows
-    int kv_len;     // admissible keys (before any causal cut)
+    int kv_len;     // admissible keys of the range (before any causal cut)
+    int delta;      // causal: key j of the range admissible for row i iff j <= i + delta
 };
 
-template <int D>
-__device__ __forceinline__ Rows rows_of(const Params& p, int b, int h, int g) {
+// GEN = false: the [B][H][N][d] layout with Nk = N, one key range, delta = 0
+// (the general fields are then not read).
+template <int D, bool GEN>
+__device__ __forceinline__ Rows rows_of(const Params& p, int b, int h, int g, int split) {
     Rows r;
-    if (p.cu_seqlens == nullptr) {
-        r.q = (size_t)(b * p.H + h) * p.N * D;
-        r.kv = (size_t)(b * p.Hkv + g) * p.N * D;
-        r.lse = (size_t)(b * p.H + h) * p.N;
-        r.q_stride = D;
-        r.kv_stride = D;
-        r.n_q = p.N;
+    if (!GEN) {
         int kv_len = p.N;
         if (p.key_lens != nullptr) {
             const int kl = p.key_lens[b];
             kv_len = kl < 0 ? 0 : (kl > p.N ? p.N : kl);
         }
+        r.q = (size_t)(b * p.H + h) * p.N * D;
+        r.o = r.q;
+        r.kv = (size_t)(b * p.Hkv + g) * p.N * D;
+        r.lse = (size_t)(b * p.H + h) * p.N;
+        r.q_stride = D;
+        r.kv_stride = D;
+        r.n_q = p.N;
         r.kv_len = kv_len;
+        r.delta = 0;
+    } else if (p.cu_seqlens == nullptr) {
+        const int k0 = split * p.chunk;  // the range's first key
+        const int k1 = p.splits > 1 ? min(p.Nk, k0 + p.chunk) : p.Nk;
+        int kv_len = p.Nk;
+        if (p.key_lens != nullptr) {
+            const int kl = p.key_lens[b];
+            kv_len = kl < 0 ? 0 : (kl > p.Nk ? p.Nk : kl);
+        }
+        r.q = (size_t)(b * p.H + h) * p.N * D;
+        r.o = (size_t)split * p.B * p.H * p.N * D + r.q;
+        r.kv = ((size_t)(b * p.Hkv + g) * p.Nk + k0) * D;
+        r.lse = (size_t)split * p.B * p.H * p.N + (size_t)(b * p.H + h) * p.N;
+        r.q_stride = D;
+        r.kv_stride = D;
+        r.n_q = p.N;
+        r.kv_len = max(min(kv_len, k1) - k0, 0);
+        r.delta = p.delta - k0;
     } else {
         const int s0 = min(max(p.cu_seqlens[b], 0), p.total);
         const int s1 = min(max(p.cu_seqlens[b + 1], s0), p.total);
         const int len = min(s1 - s0, p.N);
         r.q = ((size_t)s0 * p.H + h) * D;
+        r.o = r.q;
         r.kv = ((size_t)s0 * p.Hkv + g) * D;
         r.lse = (size_t)h * p.total + s0;
         r.q_stride = p.H * D;
         r.kv_stride = p.Hkv * D;
         r.n_q = len;
         r.kv_len = len;
+        r.delta = 0;
     }
     return r;
 }

@@ -337,7 +337,7 @@ struct Lds {
 // disjoint key sets are combined by the softmax-merge rule (unite.ai page,
 // section "闪电注意力的数学原理", formula 2): m = max(m0, m1), each side scaled
 // by 2^(m_g − m).  It doubles the waves per SIMD when the grid alone cannot.
-template <int D, bool CAUSAL, int KSPLIT>
+template <int D, bool CAUSAL, int KSPLIT, bool GEN>
 __device__ __forceinline__ void attend_tile(const Params& p, const Tile& t, const Lds<D, KSPLIT>& lds) {
     using G = Geo<D>;
     constexpr int BC = G::BC;
@@ -354,12 +354,13 @@ __device__ __forceinline__ void attend_tile(const Params& p, const Tile& t, cons
     const int qrow = q0w + ql;
     const int g = t.h / (p.H / p.Hkv);
 
-    const Rows R = rows_of<D>(p, t.b, t.h, g);
+    const Rows R = rows_of<D, GEN>(p, t.b, t.h, g, t.split);
     if (q0 >= R.n_q) return;  // (packed layout: past the end of a shorter sequence)
     const int kv_len = R.kv_len;
+    const int dq = GEN ? R.delta : 0;  // causal: key j admissible for row i iff j <= i + dq
     // keys this workgroup looks at: the admissible ones, cut under a causal
     // mask at the tile's last query row
-    const int kv_hi = CAUSAL ? min(kv_len, min(q0 + kBR, R.n_q)) : kv_len;
+    const int kv_hi = CAUSAL ? min(kv_len, max(min(q0 + kBR, R.n_q) + dq, 0)) : kv_len;
     const int ntiles = (kv_hi + BC - 1) / BC;
     const int niters = (ntiles + KSPLIT - 1) / KSPLIT;  // tile it = KSPLIT·j + grp
     const int ks = R.kv_stride;
@@ -424,10 +425,10 @@ __device__ __forceinline__ void attend_tile(const Params& p, const Tile& t, cons
             if (it + KSPLIT < ntiles) load_tile<D>(o, next, kb, vb, kv0 + KSPLIT * BC, kv_len, ks, wave);
             if (MODE == 1) {
                 tile<D, CAUSAL, 1>(w, cur, o, qf, c2, false, kv0, kv_len, qrow, hl, false);
-            } else if (it < ntiles && !(CAUSAL && kv0 > q0w + 31)) {
+            } else if (it < ntiles && !(CAUSAL && kv0 > q0w + 31 + dq)) {
                 // (under a causal mask a wave whose rows all precede the tile skips it)
-                const bool masked = (kv0 + BC > kv_len) || (CAUSAL && kv0 + BC - 1 > q0w);
-                tile<D, CAUSAL, MODE>(w, cur, o, qf, c2, masked, kv0, kv_len, qrow, hl, j == 0);
+                const bool masked = (kv0 + BC > kv_len) || (CAUSAL && kv0 + BC - 1 > q0w + dq);
+                tile<D, CAUSAL, MODE>(w, cur, o, qf, c2, masked, kv0, kv_len, qrow + dq, hl, j == 0);
             }
             wait_loads();
             __syncthreads();
@@ -452,7 +453,7 @@ __device__ __forceinline__ void attend_tile(const Params& p, const Tile& t, cons
         };
         // Tiles before n_full are unmasked for every wave of the workgroup;
         // iterations before j_full only touch such tiles in every group.
-        const int n_full = min(ntiles, (CAUSAL ? min(q0, kv_len) : kv_len) / BC);
+        const int n_full = min(ntiles, (CAUSAL ? min(max(q0 + dq, 0), kv_len) : kv_len) / BC);
         if (exact_all) {
             run_any(std::integral_constant<int, 2>{}, 0, niters);
         } else {
@@ -506,16 +507,27 @@ __device__ __forceinline__ void attend_tile(const Params& p, const Tile& t, cons
     const float l_tot = pair_sum(w.l_run);
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
     if (qrow < R.n_q) {
-        uint16_t* op = static_cast<uint16_t*>(p.o) + R.q + (size_t)qrow * R.q_stride;
+        if (GEN && p.o_f32 != nullptr) {  // a partial result, kept in fp32
+            float* op = p.o_f32 + R.o + (size_t)qrow * R.q_stride;
 #pragma unroll
-        for (int db = 0; db < G::DBLK; ++db)
+            for (int db = 0; db < G::DBLK; ++db)
 #pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                uint2 v;
-                v.x = pack_bf16x2(w.acc[db][4 * a] * inv, w.acc[db][4 * a + 1] * inv);
-                v.y = pack_bf16x2(w.acc[db][4 * a + 2] * inv, w.acc[db][4 * a + 3] * inv);
-                *reinterpret_cast<uint2*>(op + db * 32 + a * 8 + hl * 4) = v;
-            }
+                for (int a = 0; a < 4; ++a)
+                    *reinterpret_cast<float4*>(op + db * 32 + a * 8 + hl * 4) =
+                        make_float4(w.acc[db][4 * a] * inv, w.acc[db][4 * a + 1] * inv, w.acc[db][4 * a + 2] * inv,
+                                    w.acc[db][4 * a + 3] * inv);
+        } else {
+            uint16_t* op = static_cast<uint16_t*>(p.o) + R.o + (size_t)qrow * R.q_stride;
+#pragma unroll
+            for (int db = 0; db < G::DBLK; ++db)
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    uint2 v;
+                    v.x = pack_bf16x2(w.acc[db][4 * a] * inv, w.acc[db][4 * a + 1] * inv);
+                    v.y = pack_bf16x2(w.acc[db][4 * a + 2] * inv, w.acc[db][4 * a + 3] * inv);
+                    *reinterpret_cast<uint2*>(op + db * 32 + a * 8 + hl * 4) = v;
+                }
+        }
         if (hl == 0) {
             const float lse = l_tot > 0.f ? (w.m_run + log2f(l_tot)) * kLn2 : kNegInf;
             p.lse[R.lse + qrow] = lse;
@@ -531,9 +543,10 @@ __device__ __forceinline__ void attend_tile(const Params& p, const Tile& t, cons
 // …), so every workgroup — and with one workgroup per CU every CU — gets
 // about the same total work.  Returns false when workgroup `blockIdx.x` has
 // no item of round `i`.
+template <bool GEN>
 __device__ __forceinline__ bool persistent_item(const Params& p, int i, Tile* t) {
     const int G = gridDim.x, w = blockIdx.x;
-    const int heads = p.B * p.H;  // head index hb = h·B + b
+    const int heads = p.splits * p.B * p.H;  // (split, h, b) index hb = (split·H + h)·B + b
     const int T = p.q_tiles;
     int h0, nh, nwg, k;
     if (heads >= kXcds && G >= kXcds) {
@@ -550,43 +563,59 @@ __device__ __forceinline__ bool persistent_item(const Params& p, int i, Tile* t)
     }
     const int64_t r = (i & 1) ? (int64_t)(i + 1) * nwg - 1 - k : (int64_t)i * nwg + k;
     if (r >= (int64_t)nh * T) return false;
-    const int hb = h0 + (int)(r % nh);
+    const int shb = h0 + (int)(r % nh);
     t->tile = T - 1 - (int)(r / nh);
+    t->split = 0;
+    int hb = shb;
+    if (GEN && p.splits > 1) {
+        t->split = shb / (p.H * p.B);
+        hb = shb - t->split * (p.H * p.B);
+    }
     t->h = hb / p.B;
     t->b = hb - t->h * p.B;
     return true;
 }
 
-template <int D, bool CAUSAL, int KSPLIT, bool PERSIST>
+// GEN: the general form (packed sequences, key ranges of their own or split,
+// a causal diagonal offset, fp32 partial output); the plain form reads none
+// of those fields.
+template <int D, bool CAUSAL, int KSPLIT, bool PERSIST, bool GEN>
 __global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT == 1 ? (D == 64 ? 3 : 2) : 1) void attn_fwd_bf16_kernel(Params p) {
     __shared__ __attribute__((aligned(16))) char s0[KSPLIT * Geo<D>::STAGE];
     __shared__ __attribute__((aligned(16))) char s1[KSPLIT * Geo<D>::STAGE];
     const Lds<D, KSPLIT> lds{s0, s1};
     if (!PERSIST) {
-        attend_tile<D, CAUSAL, KSPLIT>(p, map_workgroup<CAUSAL>(p), lds);
+        attend_tile<D, CAUSAL, KSPLIT, GEN>(p, map_workgroup<CAUSAL, GEN>(p), lds);
         return;
     }
     Tile t;
-    for (int i = 0; persistent_item(p, i, &t); ++i) {
+    for (int i = 0; persistent_item<GEN>(p, i, &t); ++i) {
         if (i > 0) __syncthreads();  // the previous item's LDS traffic is done
-        attend_tile<D, CAUSAL, KSPLIT>(p, t, lds);
+        attend_tile<D, CAUSAL, KSPLIT, GEN>(p, t, lds);
+    }
+}
+
+template <int D, bool CAUSAL, bool GEN>
+void launch_g(const Params& p, const Schedule& sc, hipStream_t stream) {
+    const dim3 grid((unsigned)sc.grid);
+    if (sc.ksplit == 2) {
+        if (sc.persistent)
+            hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, 2, true, GEN>), grid, dim3(2 * kThreads), 0, stream, p);
+        else
+            hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, 2, false, GEN>), grid, dim3(2 * kThreads), 0, stream, p);
+    } else {
+        if (sc.persistent)
+            hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, 1, true, GEN>), grid, dim3(kThreads), 0, stream, p);
+        else
+            hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, 1, false, GEN>), grid, dim3(kThreads), 0, stream, p);
     }
 }
 
 template <int D, bool CAUSAL>
 void launch_d(const Params& p, const Schedule& sc, hipStream_t stream) {
-    const dim3 grid((unsigned)sc.grid);
-    if (sc.ksplit == 2) {
-        if (sc.persistent)
-            hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, 2, true>), grid, dim3(2 * kThreads), 0, stream, p);
-        else
-            hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, 2, false>), grid, dim3(2 * kThreads), 0, stream, p);
-    } else {
-        if (sc.persistent)
-            hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, 1, true>), grid, dim3(kThreads), 0, stream, p);
-        else
-            hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, 1, false>), grid, dim3(kThreads), 0, stream, p);
-    }
+    const bool gen = p.cu_seqlens != nullptr || p.splits > 1 || p.o_f32 != nullptr || p.delta != 0 || p.Nk != p.N;
+    if (gen) launch_g<D, CAUSAL, true>(p, sc, stream);
+    else launch_g<D, CAUSAL, false>(p, sc, stream);
 }
 
 }  // namespace

@@ -14,7 +14,7 @@
  *     lse[b,h,i] = m_i + ln ℓ_i   (natural log).
  * A row with no admissible key (key_len_b == 0) gets o = 0 and lse = -inf.
  * The N x N score matrix is never written to memory; the library allocates
- * nothing and needs no workspace.
+ * nothing (only the split-KV forward takes a caller-owned workspace).
  *
  * Layouts (all contiguous, row-major, element strides implied by the sizes):
  *     q, o : [B][H][N][d]      k, v : [B][Hkv][N][d]      lse : [B][H][N] fp32
@@ -41,6 +41,7 @@
 #ifndef ATTN_H
 #define ATTN_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -54,8 +55,12 @@ typedef enum {
     ATTN_ERR_HEAD_DIM = 3,  /* d is not 64 or 128                                 */
     ATTN_ERR_ALIGN = 4,     /* a pointer is not 16-byte aligned                   */
     ATTN_ERR_SCALE = 5,     /* scale is NaN or infinite                           */
-    ATTN_ERR_HIP = 6        /* the kernel launch failed (hipGetLastError)         */
+    ATTN_ERR_HIP = 6,       /* the kernel launch failed (hipGetLastError)         */
+    ATTN_ERR_WORKSPACE = 7  /* split-KV workspace NULL or too small               */
 } attn_status;
+
+/* Most key ranges one split-KV call may use. */
+#define ATTN_MAX_SPLITS 64
 
 /* bf16 q, k, v, o (raw 16-bit bfloat16 storage); fp32 lse.  QKᵀ and P·V run on
  * bf16 matrix cores with fp32 accumulation; the softmax runs in fp32; P is
@@ -91,6 +96,60 @@ int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float
 int attn_fwd_varlen_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                          const int32_t* cu_seqlens, int B, int H, int Hkv, int total, int max_seqlen,
                          int d, float scale, int causal, void* stream);
+
+/* Split-KV (the key range of every query cut into pieces whose partial
+ * results are combined afterwards: the softmax-merge rule of the unite.ai
+ * page, section "闪电注意力的数学原理", formula 2, read as LSE = ln Σ_s e^{LSE_s},
+ * O = Σ_s e^{LSE_s − LSE}·O_s; the same page's FlashAttention-2 section counts
+ * parallelism over the sequence among its improvements).
+ *
+ * attn_fwd_partial_bf16: attention of Nq queries over ONE block of Nk keys.
+ * q [B][H][Nq][d] and k, v [B][Hkv][Nk][d] bf16; query i sits at position
+ * q_offset + i and key j at k_offset + j of the whole sequence, and under a
+ * causal mask key j is admissible for query i iff k_offset + j <= q_offset + i
+ * (no mask: every key of the block).  Writes the block's own normalised
+ * result: o_part [B][H][Nq][d] fp32 (o = Σ_j P_ij v_j / Σ_j P_ij over the
+ * block's admissible keys) and lse_part [B][H][Nq] fp32; a row with no
+ * admissible key in the block gets o_part = 0 and lse_part = -inf.  Nk == 0
+ * is allowed (every row empty; k and v may then be NULL).  Other checks,
+ * limits (with N = Nq, and Nk·d·4 below 2^31) and status codes as
+ * attn_fwd_bf16.  Enqueued on `stream`, not waited on. */
+int attn_fwd_partial_bf16(const void* q, const void* k, const void* v, float* o_part, float* lse_part,
+                          int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                          int q_offset, int k_offset, void* stream);
+
+/* attn_merge: combines S partial results over disjoint key sets of the same
+ * queries.  o_parts fp32 [S][B][H][N][d] and lse_parts fp32 [S][B][H][N]
+ * (as written by attn_fwd_partial_bf16); o is [B][H][N][d], bf16 when
+ * o_bf16 == 1 and fp32 when 0 (so that merges can be chained), lse fp32
+ * [B][H][N].  Parts with lse = -inf take no part; a row empty in every part
+ * gets o = 0, lse = -inf.  S >= 1, B >= 0, H >= 1, N >= 0, d in {64, 128};
+ * all pointers device, 16-byte aligned; o must not overlap the inputs.
+ * Enqueued on `stream`, not waited on. */
+int attn_merge(const float* o_parts, const float* lse_parts, int S, int B, int H, int N, int d,
+               void* o, int o_bf16, float* lse, void* stream);
+
+/* attn_fwd_splitkv_bf16: attention of Nq queries over Nk keys, the keys cut
+ * into num_splits (1 .. ATTN_MAX_SPLITS) ranges of ceil(Nk / num_splits) keys
+ * rounded up to a multiple of 128 (so fewer ranges may result), one fp32
+ * partial result per range, merged as in attn_merge: two kernels on
+ * `stream`.  q, o [B][H][Nq][d] and k, v [B][Hkv][Nk][d] bf16, lse
+ * [B][H][Nq] fp32; positions and the causal rule as attn_fwd_partial_bf16
+ * (self-attention: Nq = Nk = N, q_offset = k_offset = 0, which is
+ * attn_fwd_bf16's operation); key_lens as in attn_fwd_bf16, cutting the Nk
+ * keys.  It fills the GPU when B·H·ceil(Nq/128) is small (few queries over
+ * many keys).  workspace: caller-owned device memory of at least
+ * attn_splitkv_workspace_bytes(B, H, Nq, d, num_splits) bytes, 16-byte
+ * aligned, overwritten (ATTN_ERR_WORKSPACE if NULL or too small; unused, and
+ * may be NULL, when a single range results).  Checks and limits as
+ * attn_fwd_partial_bf16, then num_splits, then the workspace. */
+int attn_fwd_splitkv_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                          int q_offset, int k_offset, const int32_t* key_lens, int num_splits,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes attn_fwd_splitkv_bf16 needs for Nq queries (0 for invalid sizes). */
+size_t attn_splitkv_workspace_bytes(int B, int H, int Nq, int d, int num_splits);
 
 /* Backward pass, bf16 (gradients of L = Σ O ∘ dout through the operation
  * above; the attention weights are recomputed from q, k and the forward's lse

@@ -13,7 +13,9 @@ brute force over every block size); see ``tests/test_oracle_pins.py`` and
 ``tests/test_oracle_blockwise.py``; the backward pass against torch autograd,
 finite differences and invariants in ``tests/test_oracle_backward.py``; the
 packed-sequence form against brute force and invariants in
-``tests/test_oracle_varlen.py``.  No
+``tests/test_oracle_varlen.py``; the key-block partials and the S-way merge
+against brute force, the full definition and invariants in
+``tests/test_oracle_partial.py``.  No
 function here is "parity unpinned".
 """
 
@@ -21,9 +23,11 @@ from .attention import (  # noqa: F401
     admissible,
     attention,
     attention_backward,
+    attention_partial,
     attention_varlen,
     blockwise_attention,
     kv_head_of,
+    merge_many,
     merge_partials,
     merge_softmax,
     scores,

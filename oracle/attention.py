@@ -42,6 +42,8 @@ __all__ = [
     "merge_softmax",
     "attention_backward",
     "attention_varlen",
+    "attention_partial",
+    "merge_many",
 ]
 
 
@@ -301,3 +303,46 @@ def attention_varlen(q, k, v, cu_seqlens, scale, causal=False):
         O[s0:s1] = o_b[0].transpose(1, 0, 2)
         LSE[:, s0:s1] = lse_b[0]
     return O, LSE
+
+
+def attention_partial(q, k, v, scale, causal=False, q_offset=0, k_offset=0):
+    """Attention of the queries over one block of keys, normalised within the
+    block: the split-KV building block whose results the softmax-merge rule
+    (unite.ai page, section "闪电注意力的数学原理", formula 2) combines.
+
+    q: [B, H, Nq, d] with query i at position q_offset + i of the sequence;
+    k, v: [B, Hkv, Nk, d] with key j at position k_offset + j.  Under a causal
+    mask key j is admissible for query i iff k_offset + j ≤ q_offset + i (the
+    causal reading at absolute positions).  Returns (O, LSE) over the block's
+    admissible keys: O fp64 [B, H, Nq, d], LSE fp64 [B, H, Nq]; a row with no
+    admissible key gets O = 0 and LSE = −∞.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    O = np.zeros((B, H, Nq, d))
+    LSE = np.full((B, H, Nq), -np.inf)
+    rows_abs = q_offset + np.arange(Nq)
+    keys_abs = k_offset + np.arange(Nk)
+    ok = np.ones((Nq, Nk), dtype=bool)
+    if causal:
+        ok &= keys_abs[None, :] <= rows_abs[:, None]
+    for b in range(B):
+        for h in range(H):
+            g = kv_head_of(h, H, Hkv)
+            s = np.where(ok, scores(q[b, h], k[b, g], scale), -np.inf)
+            p, m, ell = softmax_rows(s)
+            O[b, h] = p @ v[b, g]
+            live = m > -np.inf
+            LSE[b, h] = np.where(live, m + np.log(np.where(live, ell, 1.0)), -np.inf)
+    return O, LSE
+
+
+def merge_many(o_parts, lse_parts):
+    """Combine S partial results (o_parts [S, ..., d], lse_parts [S, ...]) over
+    disjoint key sets by folding the two-way merge ``merge_partials`` (the
+    merge is associative: LSE = ln Σ_s e^{LSE_s}, O = Σ_s e^{LSE_s − LSE} O_s)."""
+    o, lse = _f64(o_parts[0]), _f64(lse_parts[0])
+    for s in range(1, len(o_parts)):
+        o, lse = merge_partials(o, lse, o_parts[s], lse_parts[s])
+    return o, lse

@@ -183,3 +183,89 @@ def test_python_forward_varlen_rejects_bad_tensors():
         attn.forward_varlen(q, q, q, cu, 8)              # CPU tensors
     with pytest.raises(ValueError):
         attn.forward_varlen(q[None], q, q, cu, 8)        # wrong rank
+
+
+PART_GOOD = dict(q=P, k=P * 2, v=P * 3, o=P * 4, lse=P * 5, B=2, H=4, Hkv=2, Nq=100, Nk=300, d=64, scale=0.125,
+                 causal=1, q_offset=200, k_offset=0, stream=None)
+
+
+def call_partial(**over):
+    a = dict(PART_GOOD, **over)
+    return attn.attn_fwd_partial_bf16(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"], a["Nq"],
+                                      a["Nk"], a["d"], a["scale"], a["causal"], a["q_offset"], a["k_offset"],
+                                      a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(d=32), attn.ATTN_ERR_HEAD_DIM),
+    (dict(Nk=-1), attn.ATTN_ERR_SHAPE),
+    (dict(Nq=-1), attn.ATTN_ERR_SHAPE),
+    (dict(Nk=2**23), attn.ATTN_ERR_SHAPE),
+    (dict(H=4, Hkv=3), attn.ATTN_ERR_SHAPE),
+    (dict(scale=math.inf), attn.ATTN_ERR_SCALE),
+    (dict(k=None), attn.ATTN_ERR_NULL),
+    (dict(o=None), attn.ATTN_ERR_NULL),
+    (dict(v=P + 8), attn.ATTN_ERR_ALIGN),
+    (dict(B=0, q=None, k=None, v=None, o=None, lse=None), attn.ATTN_OK),
+    (dict(Nq=0, q=None, k=None, v=None, o=None, lse=None), attn.ATTN_OK),
+])
+def test_partial_host_validation(over, status):
+    assert call_partial(**over) == status
+
+
+MERGE_GOOD = dict(op=P, lp=P * 2, S=3, B=2, H=4, N=100, d=128, o=P * 3, o_bf16=1, lse=P * 4, stream=None)
+
+
+def call_merge(**over):
+    a = dict(MERGE_GOOD, **over)
+    return attn.attn_merge(a["op"], a["lp"], a["S"], a["B"], a["H"], a["N"], a["d"], a["o"], a["o_bf16"], a["lse"],
+                           a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(S=0), attn.ATTN_ERR_SHAPE),
+    (dict(o_bf16=2), attn.ATTN_ERR_SHAPE),
+    (dict(H=0), attn.ATTN_ERR_SHAPE),
+    (dict(d=96), attn.ATTN_ERR_HEAD_DIM),
+    (dict(op=None), attn.ATTN_ERR_NULL),
+    (dict(lse=None), attn.ATTN_ERR_NULL),
+    (dict(lp=P + 4), attn.ATTN_ERR_ALIGN),
+    (dict(N=0, op=None, lp=None, o=None, lse=None), attn.ATTN_OK),
+])
+def test_merge_host_validation(over, status):
+    assert call_merge(**over) == status
+
+
+def test_splitkv_workspace_bytes():
+    assert attn.attn_splitkv_workspace_bytes(2, 4, 1000, 64, 3) == 3 * 2 * 4 * 1000 * 65 * 4
+    assert attn.attn_splitkv_workspace_bytes(2, 4, 1000, 64, 0) == 0
+    assert attn.attn_splitkv_workspace_bytes(2, 4, 1000, 64, attn.ATTN_MAX_SPLITS + 1) == 0
+    assert attn.attn_splitkv_workspace_bytes(2, 4, 1000, 96, 2) == 0
+
+
+SPLIT_GOOD = dict(GOOD, Nq=200, Nk=1000, q_offset=800, k_offset=0, ns=4, ws=P * 8,
+                  wsb=attn.attn_splitkv_workspace_bytes(1, 4, 200, 64, 4))
+
+
+def call_split(**over):
+    a = dict(SPLIT_GOOD, **over)
+    return attn.attn_fwd_splitkv_bf16(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"], a["Nq"],
+                                      a["Nk"], a["d"], a["scale"], a["causal"], a["q_offset"], a["k_offset"],
+                                      a["key_lens"], a["ns"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(ns=0), attn.ATTN_ERR_SHAPE),
+    (dict(ns=attn.ATTN_MAX_SPLITS + 1), attn.ATTN_ERR_SHAPE),
+    (dict(d=80), attn.ATTN_ERR_HEAD_DIM),
+    (dict(q=None), attn.ATTN_ERR_NULL),
+    (dict(ws=None), attn.ATTN_ERR_WORKSPACE),
+    (dict(wsb=100), attn.ATTN_ERR_WORKSPACE),
+    (dict(ws=P * 8 + 4), attn.ATTN_ERR_ALIGN),
+    (dict(Nk=-3), attn.ATTN_ERR_SHAPE),
+    (dict(B=0, q=None, k=None, v=None, o=None, lse=None, ws=None), attn.ATTN_OK),
+    # one range (Nk <= 128): the plain forward pass, no workspace needed
+    (dict(Nk=100, ws=None, wsb=0, q=None), attn.ATTN_ERR_NULL),
+])
+def test_splitkv_host_validation(over, status):
+    assert call_split(**over) == status

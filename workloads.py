@@ -82,6 +82,13 @@ VARLEN = dict(name="packed varlen B8 lengths U[4096,8192] Hq32 Hkv8 d128 causal 
               B=8, N=8192, H=32, Hkv=8, d=128, causal=True, seed=6)
 
 
+# Split-KV: the last 512 positions of a 32768-token sequence (a chunk of
+# queries) over its whole key cache, causal, GQA, in 16 key ranges: only
+# 32 heads x 4 query tiles of work without the split.
+SPLITKV = dict(name="split-KV chunk Nq512 over Nk32768 Hq32 Hkv8 d128 causal, 16 ranges, bf16",
+               B=1, H=32, Hkv=8, Nq=512, Nk=32768, d=128, causal=True, splits=16, seed=7)
+
+
 def varlen_lengths(B, lo, hi, seed):
     """B sequence lengths drawn uniformly from the integers lo .. hi inclusive
     (a torch.Generator('cpu') seeded with ``seed``)."""
