@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 METRIC = "attention fwd TFLOP/s (4·B·H·N²·d) and % of bf16 MFMA peak, 1 MI355X"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 matrix, published
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA, published
 HEADLINE = 2
 
 
@@ -152,6 +153,30 @@ class Runner:
         return start.elapsed_time(end) / steps
 
 
+class Fp8Runner(Runner):
+    """A workload's fp8 form (attn_fwd_fp8: e4m3 q, k and V transposed, one
+    descale factor each) resident on the GPU."""
+
+    def __init__(self, w, dev):
+        import torch
+
+        import exact_tiled_attention_14_amd as attn
+        from workloads import make_fp8
+
+        self.w = w
+        q8, k8, _, vt8, ds, kl = make_fp8(w.B, w.H, w.Hkv, w.N, w.d, seed=100 + w.seed, padded=w.padded)
+        self.key_lens_host = None if kl is None else kl.tolist()
+        self.q, self.k, self.vt = q8.to(dev), k8.to(dev), vt8.to(dev)
+        self.kl = None if kl is None else kl.to(dev)
+        self.o = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+        self.stream = torch.cuda.current_stream(dev)
+        self.fn = attn.attn_fwd_fp8
+        self.args = (self.q.data_ptr(), self.k.data_ptr(), self.vt.data_ptr(), self.o.data_ptr(),
+                     self.lse.data_ptr(), ds[0], ds[1], ds[2], w.B, w.H, w.Hkv, w.N, w.d, w.scale, int(w.causal),
+                     None if self.kl is None else self.kl.data_ptr(), self.stream.cuda_stream)
+
+
 class VarlenRunner(Runner):
     """The packed variable-length batch (attn_fwd_varlen_bf16) resident on the GPU."""
 
@@ -271,6 +296,7 @@ def main():
     ap.add_argument("--no-backward", action="store_true", help="skip timing the backward pass")
     ap.add_argument("--no-varlen", action="store_true", help="skip timing the packed variable-length batch")
     ap.add_argument("--no-splitkv", action="store_true", help="skip timing the split-KV shape")
+    ap.add_argument("--no-fp8", action="store_true", help="skip timing the fp8 forward")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 3 device-to-device copies of MIB MiB (a plain copy kernel of known "
                          "traffic, to calibrate the FETCH_SIZE / WRITE_SIZE counters)")
@@ -380,6 +406,21 @@ def main():
                           "algorithmic_tflops": round(a / (m * 1e-3) / 1e12, 2),
                           "frac_of_bf16_peak": round(a / (m * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
         del vr
+
+    if not args.no_fp8:
+        # fp8 forms of the long workloads (same shapes, masks and key lengths)
+        fp8 = {}
+        for wid in (4, 5):
+            ww = WORKLOADS[wid]
+            fr = Fp8Runner(ww, dev)
+            steps = max(10, min(args.steps, 50))
+            m = fr.time(steps, 3)
+            a = algorithmic_flops(ww, fr.key_lens_host)
+            fp8[str(wid)] = {"workload": ww.name.replace("bf16", "fp8 e4m3"), "ms": round(m, 4), "steps": steps,
+                             "algorithmic_tflops": round(a / (m * 1e-3) / 1e12, 2),
+                             "frac_of_fp8_peak": round(a / (m * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4)}
+            del fr
+        line["fp8"] = fp8
 
     if not args.no_splitkv:
         from workloads import SPLITKV

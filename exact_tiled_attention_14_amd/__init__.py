@@ -18,7 +18,7 @@ import os
 
 __all__ = [
     "AttnError", "attn_fwd", "attn_fwd_bf16", "attn_fwd_f32", "attn_fwd_varlen_bf16", "attn_bwd_bf16",
-    "attn_fwd_partial_bf16", "attn_merge", "attn_fwd_splitkv_bf16", "attn_splitkv_workspace_bytes",
+    "attn_fwd_fp8", "forward_fp8", "attn_fwd_partial_bf16", "attn_merge", "attn_fwd_splitkv_bf16", "attn_splitkv_workspace_bytes",
     "attn_status_str", "forward", "forward_varlen", "forward_partial", "merge", "forward_splitkv", "backward",
     "library_path", "load_library", "ATTN_ERR_WORKSPACE", "ATTN_MAX_SPLITS",
     "ATTN_OK", "ATTN_ERR_NULL", "ATTN_ERR_SHAPE", "ATTN_ERR_HEAD_DIM", "ATTN_ERR_ALIGN",
@@ -46,6 +46,7 @@ ENTRY_POINTS = {
     "attn_fwd_splitkv_bf16": ([_P] * 5 + [_I] * 6 + [ctypes.c_float, _I, _I, _I, _P, _I, _P, ctypes.c_size_t, _P],
                               ctypes.c_int),
     "attn_splitkv_workspace_bytes": ([_I] * 5, ctypes.c_size_t),
+    "attn_fwd_fp8": ([_P] * 5 + [ctypes.c_float] * 3 + [_I] * 5 + [ctypes.c_float, _I, _P, _P], ctypes.c_int),
     "attn_bwd_bf16": ([_P] * 10 + [_I, _I, _I, _I, _I, ctypes.c_float, _I, _P, _P], ctypes.c_int),
     "attn_status_str": ([_I], ctypes.c_char_p),
 }
@@ -102,6 +103,12 @@ def attn_fwd_partial_bf16(q, k, v, o_part, lse_part, B, H, Hkv, Nq, Nk, d, scale
                           stream):
     return load_library().attn_fwd_partial_bf16(q, k, v, o_part, lse_part, B, H, Hkv, Nq, Nk, d, scale, causal,
                                                 q_offset, k_offset, stream)
+
+
+def attn_fwd_fp8(q, k, vt, o, lse, q_descale, k_descale, v_descale, B, H, Hkv, N, d, scale, causal, key_lens,
+                 stream):
+    return load_library().attn_fwd_fp8(q, k, vt, o, lse, q_descale, k_descale, v_descale, B, H, Hkv, N, d, scale,
+                                       causal, key_lens, stream)
 
 
 def attn_merge(o_parts, lse_parts, S, B, H, N, d, o, o_bf16, lse, stream):
@@ -216,6 +223,40 @@ def _check_bf16(**tensors):
     for name, t in tensors.items():
         if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous bfloat16 GPU tensor")
+
+
+def forward_fp8(q, k, vt, q_descale, k_descale, v_descale, *, scale=None, causal=False, key_lens=None,
+                stream=None):
+    """FP8 forward: q [B, H, N, d], k [B, Hkv, N, d], vt [B, Hkv, d, N] (V
+    transposed) as torch.float8_e4m3fn GPU tensors standing for descale ·
+    stored value.  Returns (o bf16 [B, H, N, d], lse fp32 [B, H, N])."""
+    import torch
+
+    if q.dim() != 4 or k.dim() != 4 or vt.dim() != 4:
+        raise ValueError("q, k, vt must be 4-D")
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    if tuple(k.shape) != (B, Hkv, N, d) or tuple(vt.shape) != (B, Hkv, d, N):
+        raise ValueError("shape mismatch: k must be [B, Hkv, N, d] and vt [B, Hkv, d, N]")
+    for name, t in (("q", q), ("k", k), ("vt", vt)):
+        if t.dtype != torch.float8_e4m3fn or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float8_e4m3fn GPU tensor")
+    if key_lens is not None:
+        if key_lens.dtype != torch.int32 or not key_lens.is_cuda or key_lens.numel() != B:
+            raise ValueError("key_lens must be an int32 GPU tensor with B entries")
+        key_lens = key_lens.contiguous()
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = attn_fwd_fp8(q.data_ptr(), k.data_ptr(), vt.data_ptr(), o.data_ptr(), lse.data_ptr(), float(q_descale),
+                      float(k_descale), float(v_descale), B, H, Hkv, N, d, float(scale), int(bool(causal)),
+                      key_lens.data_ptr() if key_lens is not None else None, stream)
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_fp8")
+    return o, lse
 
 
 def forward_partial(q, k, v, *, q_offset=0, k_offset=0, scale=None, causal=False, stream=None):

@@ -11,7 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libattn.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
-SOURCES = ["attn_api.hip", "attn_fwd_bf16.hip", "attn_fwd_f32.hip", "attn_bwd_bf16.hip", "attn_merge.hip"]
+SOURCES = ["attn_api.hip", "attn_fwd_bf16.hip", "attn_fwd_f32.hip", "attn_bwd_bf16.hip", "attn_merge.hip", "attn_fwd_fp8.hip"]
 
 # Packed fp32 VALU forms are disabled: the code below is written for plain
 # fp32 VALU and MFMA only.

@@ -11,6 +11,7 @@ namespace attn {
 hipError_t launch_fwd_bf16(const Params& p, int d, bool causal, const Schedule& sc, hipStream_t stream);
 hipError_t launch_fwd_f32(const Params& p, int d, bool causal, hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool causal, hipStream_t stream);
+hipError_t launch_fwd_fp8(const Params& p, int d, bool causal, hipStream_t stream);
 hipError_t launch_merge(const float* o_parts, const float* lse_parts, int S, int64_t rows, int d, void* o,
                         bool o_bf16, float* lse, hipStream_t stream);
 }  // namespace attn
@@ -61,6 +62,7 @@ int validate(const void* q, const void* k, const void* v, const void* o, const v
     p->chunk = N;
     p->delta = 0;
     p->o_f32 = nullptr;
+    p->o_scale = 1.0f;
     return ATTN_OK;
 }
 
@@ -275,6 +277,25 @@ int attn_fwd_splitkv_bf16(const void* q, const void* k, const void* v, void* o, 
     hipError_t e = attn::launch_fwd_bf16(p, d, causal != 0, schedule_bf16(p, causal != 0), hs);
     if (e != hipSuccess) return ATTN_ERR_HIP;
     e = attn::launch_merge(o_parts, lse_parts, S, (int64_t)B * H * Nq, d, o, true, lse, hs);
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int attn_fwd_fp8(const void* q, const void* k, const void* vt, void* o, float* lse,
+                 float q_descale, float k_descale, float v_descale,
+                 int B, int H, int Hkv, int N, int d, float scale, int causal,
+                 const int32_t* key_lens, void* stream) {
+    if (N >= 0 && N % 16 != 0) return ATTN_ERR_SHAPE;  // Vᵀ rows are read in 16-byte pieces
+    if (!isfinite(q_descale) || !isfinite(k_descale) || !isfinite(v_descale)) return ATTN_ERR_SCALE;
+    attn::Params p;
+    bool empty = false;
+    // the score scale folds in both descale factors
+    const float s_eff = scale * q_descale * k_descale;
+    const int st = validate(q, k, vt, o, lse, B, H, Hkv, N, d, isfinite(scale) ? s_eff : scale, causal, key_lens,
+                            &p, &empty);
+    if (st != ATTN_OK || empty) return st;
+    p.o_scale = v_descale;
+    (void)hipGetLastError();
+    const hipError_t e = attn::launch_fwd_fp8(p, d, causal != 0, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

@@ -51,6 +51,7 @@ struct Params {
     int chunk;
     int delta;
     float* o_f32;
+    float o_scale;  // fp8 forward: O is multiplied by this (the V descale factor)
 };
 
 // Backward pass: the forward's problem (q, k, v, lse, sizes, key_lens) plus

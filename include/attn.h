@@ -97,6 +97,25 @@ int attn_fwd_varlen_bf16(const void* q, const void* k, const void* v, void* o, f
                          const int32_t* cu_seqlens, int B, int H, int Hkv, int total, int max_seqlen,
                          int d, float scale, int causal, void* stream);
 
+/* FP8 forward (the low-precision step of the unite.ai page, section
+ * "闪电注意力-3"): the operation above on fp8 operands.  q [B][H][N][d],
+ * k [B][Hkv][N][d] and vt [B][Hkv][d][N] (V TRANSPOSED: its rows are the d
+ * features, each over the N keys) hold OCP fp8 e4m3 bytes; the values they
+ * stand for are q_descale·q, k_descale·k, v_descale·v.  Outputs o bf16
+ * [B][H][N][d] and lse fp32 [B][H][N] as for attn_fwd_bf16, for those values.
+ * Both products run on fp8 matrix cores with fp32 accumulation; the softmax
+ * runs in fp32 and its weights are rounded to fp8 e4m3 (relative error at
+ * most 2^-4 each, after scaling by 2^7 relative to a running reference that
+ * is at most 2x below the true max, so they stay in range) before P·V; the
+ * row sums use the fp32 weights.  N must be a multiple of 16; descale
+ * factors finite; scale·q_descale·k_descale finite.  Other limits, checks
+ * and status codes as attn_fwd_bf16 (vt is checked as its v).  Padded keys
+ * (past key_lens[b]) never reach the output, NaN included. */
+int attn_fwd_fp8(const void* q, const void* k, const void* vt, void* o, float* lse,
+                 float q_descale, float k_descale, float v_descale,
+                 int B, int H, int Hkv, int N, int d, float scale, int causal,
+                 const int32_t* key_lens, void* stream);
+
 /* Split-KV (the key range of every query cut into pieces whose partial
  * results are combined afterwards: the softmax-merge rule of the unite.ai
  * page, section "闪电注意力的数学原理", formula 2, read as LSE = ln Σ_s e^{LSE_s},

@@ -269,3 +269,42 @@ def call_split(**over):
 ])
 def test_splitkv_host_validation(over, status):
     assert call_split(**over) == status
+
+
+FP8_GOOD = dict(GOOD, N=64, qd=0.01, kd=0.02, vd=0.03)
+
+
+def call_fp8(**over):
+    a = dict(FP8_GOOD, **over)
+    return attn.attn_fwd_fp8(a["q"], a["k"], a["v"], a["o"], a["lse"], a["qd"], a["kd"], a["vd"], a["B"], a["H"],
+                             a["Hkv"], a["N"], a["d"], a["scale"], a["causal"], a["key_lens"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(N=60), attn.ATTN_ERR_SHAPE),           # V transposed is read in 16-byte pieces
+    (dict(d=96), attn.ATTN_ERR_HEAD_DIM),
+    (dict(qd=math.nan), attn.ATTN_ERR_SCALE),
+    (dict(vd=math.inf), attn.ATTN_ERR_SCALE),
+    (dict(scale=1e30, qd=1e30), attn.ATTN_ERR_SCALE),  # the combined score scale overflows
+    (dict(H=3, Hkv=2), attn.ATTN_ERR_SHAPE),
+    (dict(v=None), attn.ATTN_ERR_NULL),
+    (dict(k=P + 4), attn.ATTN_ERR_ALIGN),
+    (dict(B=0, q=None, k=None, v=None, o=None, lse=None), attn.ATTN_OK),
+    (dict(N=0, q=None, k=None, v=None, o=None, lse=None), attn.ATTN_OK),
+])
+def test_fp8_host_validation(over, status):
+    assert call_fp8(**over) == status
+
+
+def test_fp8_quantisation_recipe():
+    """The test-input quantiser: values within half an e4m3 step, no NaN
+    from out-of-range magnitudes, max maps to 448."""
+    import torch
+
+    from workloads import quantize_fp8
+    x = torch.tensor([0.0, 1.0, -3.0, 7.5, 1e-6])
+    s, d = quantize_fp8(x)
+    back = s.float() * d
+    assert not torch.isnan(back).any()
+    assert abs(float(s.float().abs().max()) - 448.0) == 0.0
+    assert torch.all((back - x).abs() <= x.abs() * 2.0 ** -4 + d * 2.0 ** -10)

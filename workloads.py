@@ -112,3 +112,34 @@ def make_varlen(lengths, H, Hkv, d, seed=0):
 def as_f64(t):
     """Exact fp64 numpy copy of a CPU tensor (bf16 and fp32 both embed exactly)."""
     return t.detach().to("cpu", torch.float64).numpy()
+
+
+def quantize_fp8(x):
+    """Per-tensor fp8 (OCP e4m3) quantisation of a float tensor for the fp8
+    path: descale = max|x| / 448 (e4m3's largest finite value), stored =
+    round-to-nearest-even of x / descale after clamping to ±448 (torch's cast
+    does not saturate).  Returns (stored float8_e4m3fn tensor, descale float);
+    the value a stored byte stands for is descale · stored."""
+    amax = float(x.abs().max())
+    descale = float(np.float32(amax / 448.0)) if amax > 0 else 1.0
+    stored = (x.float() / descale).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
+    return stored, descale
+
+
+def make_fp8(B, H, Hkv, N, d, seed=0, padded=False):
+    """fp8 inputs following the recipe above: q, k, v drawn as for
+    ``make_qkv`` (fp32 N(0, 1)), each quantised per tensor with
+    ``quantize_fp8``; V is also returned transposed ([B, Hkv, d, N]) as the
+    fp8 path takes it.  Returns (q8, k8, v8, vt8, (qd, kd, vd), key_lens)."""
+    g = torch.Generator("cpu").manual_seed(int(seed))
+    q = torch.randn((B, H, N, d), generator=g, dtype=torch.float32)
+    k = torch.randn((B, Hkv, N, d), generator=g, dtype=torch.float32)
+    v = torch.randn((B, Hkv, N, d), generator=g, dtype=torch.float32)
+    key_lens = None
+    if padded:
+        key_lens = torch.randint(N // 2, N + 1, (B,), generator=g, dtype=torch.int32)
+    q8, qd = quantize_fp8(q)
+    k8, kd = quantize_fp8(k)
+    v8, vd = quantize_fp8(v)
+    vt8 = v8.transpose(-1, -2).contiguous()
+    return q8, k8, v8, vt8, (qd, kd, vd), key_lens
