@@ -29,6 +29,13 @@
 // α = 2^(m_old − m_new).  Hence every P' ≤ 2^7 · 2 = 256, inside fp8 e4m3's
 // range (448), and fp8's subnormals reach P = 2^-16 of the reference.
 // Epilogue: O = v_descale · Oᵀ / ℓ (bf16), LSE = (m + log2 ℓ − 7) · ln 2.
+//
+// Data movement as in the bf16 kernel (direct HBM → LDS loads, K rows padded
+// to d + 16 bytes, Vᵀ rows of 64 keys to 80 bytes), with three LDS stages:
+// tile j + 2 is loaded while tile j is computed.  Every wave issues the same
+// number of loads per tile, so that a wait can leave exactly the newest
+// tile's loads in flight, and the barrier closing a step is a bare s_barrier
+// (the fence of __syncthreads would also wait for those loads).
 #include "attn_common.h"
 
 namespace attn {
@@ -94,29 +101,47 @@ typedef __attribute__((address_space(3))) void lds_void8;
 // One K tile (rows kv0 .. kv0 + 63, zeros past kv_len) and one Vᵀ tile
 // (columns kv0 .. kv0 + 63 of the d rows; 16-byte pieces that start at or past
 // kv_len are loaded from out of range, i.e. as zeros) into an LDS stage.
+// Every wave issues exactly KI + VI loads per tile (a wave whose share is
+// one short sends the extra load out of range, i.e. zeros, into `spare`), so
+// that the loads of one tile can be waited for while the next tile's stay in
+// flight; a tile past the end (kv0 >= kv_len) is loaded as zeros.
+constexpr uint32_t kOut8 = 0x7FFFFFF0u;
+
 template <int D>
-__device__ __forceinline__ void load_tile8(const Offsets8<D>& o, char* stage, const uint8_t* kb, const uint8_t* vt,
-                                           int kv0, int kv_len, int n_keys_row, int wave) {
+__device__ __forceinline__ void load_tile8(const Offsets8<D>& o, char* stage, char* spare, const uint8_t* kb,
+                                           const uint8_t* vt, int kv0, int kv_len, int n_keys_row, int wave) {
 #if defined(__HIP_DEVICE_COMPILE__)
     using C = Cfg8<D>;
-    const __amdgpu_buffer_rsrc_t kres = make_rsrc(kb + (size_t)kv0 * D, (uint32_t)min(kv_len - kv0, C::BC) * D);
-    const __amdgpu_buffer_rsrc_t vres = make_rsrc(vt + kv0, (uint32_t)((D - 1) * n_keys_row + C::BC));
+    const bool live = kv0 < kv_len;
+    const __amdgpu_buffer_rsrc_t kres =
+        make_rsrc(kb + (size_t)(live ? kv0 : 0) * D, live ? (uint32_t)min(kv_len - kv0, C::BC) * D : 0u);
+    const __amdgpu_buffer_rsrc_t vres = make_rsrc(vt + (live ? kv0 : 0), (uint32_t)((D - 1) * n_keys_row + C::BC));
 #pragma unroll
     for (int i = 0; i < C::KI; ++i) {
         const int t = wave + kWaves * i;
-        if (t < C::NK) __builtin_amdgcn_raw_ptr_buffer_load_lds(kres, (lds_void8*)(stage + 1024 * t), 16, o.k_src[i], 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kres, (lds_void8*)(t < C::NK ? stage + 1024 * t : spare), 16,
+                                                 t < C::NK ? o.k_src[i] : kOut8, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < C::VI; ++i) {
         const int t = wave + kWaves * i;
-        const uint32_t off = kv0 + o.v_col[i] < kv_len ? o.v_src[i] : 0x7FFFFFF0u;
-        if (t < C::NV)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(vres, (lds_void8*)(stage + C::K_BYTES + 1024 * t), 16, off, 0, 0, 0);
+        const uint32_t off = (t < C::NV && kv0 + o.v_col[i] < kv_len) ? o.v_src[i] : kOut8;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vres, (lds_void8*)(t < C::NV ? stage + C::K_BYTES + 1024 * t : spare),
+                                                 16, off, 0, 0, 0);
     }
 #endif
 }
 
-__device__ __forceinline__ void wait_loads8() { __builtin_amdgcn_s_waitcnt(0x0F70); /* vmcnt(0) */ }
+// all but the last tile's loads of this wave have landed; then a bare
+// barrier (__syncthreads would also wait for the loads still in flight)
+template <int D>
+__device__ __forceinline__ void wait_older_and_sync() {
+    constexpr int n = Cfg8<D>::KI + Cfg8<D>::VI;
+    static_assert(n < 16, "vmcnt immediate");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | n);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads are done
+    __builtin_amdgcn_s_barrier();
+}
 
 __device__ __forceinline__ float pair_max8(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -145,8 +170,12 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_fp8_kernel(Params p) {
     using C = Cfg8<D>;
     constexpr int BC = C::BC;
+    // three stages (separate objects, so the compiler can tell the loads in
+    // flight from the reads): tile j + 2 loads while tile j is computed
     __shared__ __attribute__((aligned(16))) char s0[C::STAGE];
     __shared__ __attribute__((aligned(16))) char s1[C::STAGE];
+    __shared__ __attribute__((aligned(16))) char s2[C::STAGE];
+    __shared__ __attribute__((aligned(16))) char spare[1024];
 
     const Tile t = map_workgroup<CAUSAL>(p);
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
@@ -167,7 +196,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_fp8_kernel(Params p) {
 
     Offsets8<D> o;
     o.init(wave, lane, p.N);
-    if (ntiles > 0) load_tile8<D>(o, s0, kb, vt, 0, kv_len, p.N, wave);
+    load_tile8<D>(o, s0, spare, kb, vt, 0, ntiles > 0 ? kv_len : 0, p.N, wave);
 
     // Q rows as the Sᵀ B operand: chunk c holds d = 64c + 32h .. + 31
     i32x8 qf[C::DC];
@@ -193,12 +222,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_fp8_kernel(Params p) {
     float m_run = kNegInf, l_run = 0.f;
     const float c2 = p.scale_log2;
 
-    wait_loads8();
-    __syncthreads();
+    load_tile8<D>(o, s1, spare, kb, vt, BC, ntiles > 1 ? kv_len : 0, p.N, wave);
+    wait_older_and_sync<D>();  // tile 0 (and Q) in; tile 1 may still be on its way
 
-    auto step = [&](int j, const char* cur, char* next) __attribute__((always_inline)) {
+    auto step = [&](int j, const char* cur, char* next2) __attribute__((always_inline)) {
         const int kv0 = j * BC;
-        if (j + 1 < ntiles) load_tile8<D>(o, next, kb, vt, kv0 + BC, kv_len, p.N, wave);
+        load_tile8<D>(o, next2, spare, kb, vt, kv0 + 2 * BC, j + 2 < ntiles ? kv_len : 0, p.N, wave);
         if (!(CAUSAL && kv0 > q0w + 31)) {  // (a wave whose rows all precede the tile skips it)
             const bool masked = (kv0 + BC > kv_len) || (CAUSAL && kv0 + BC - 1 > q0w);
             f32x16 s[2];
@@ -258,33 +287,37 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_fp8_kernel(Params p) {
             i32x8 pb;
 #pragma unroll
             for (int i = 0; i < 8; ++i) pb[i] = (int)pk[i];
+            // all Vᵀ operands first, so that the P·V MFMAs issue back to back
+            i32x8 va[C::DBLK];
 #pragma unroll
-            for (int db = 0; db < C::DBLK; ++db) {
-                i32x8 a = read32(cur + C::K_BYTES + o.v_rd + db * 32 * C::VROW);
-                if (masked) {
-                    // keys at or past kv_len inside a 16-byte piece that was
-                    // loaded: zero them (their P' is 0, but 0 · NaN is NaN)
+            for (int db = 0; db < C::DBLK; ++db) va[db] = read32(cur + C::K_BYTES + o.v_rd + db * 32 * C::VROW);
+            if (masked) {
+                // keys at or past kv_len inside a 16-byte piece that was
+                // loaded: zero them (their P' is 0, but 0 · NaN is NaN)
+                uint32_t keepb[8];
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const int key0 = kv0 + 32 * hl + 4 * i;
-                        uint32_t keepb = 0;
+                for (int i = 0; i < 8; ++i) {
+                    const int key0 = kv0 + 32 * hl + 4 * i;
+                    uint32_t m = 0;
 #pragma unroll
-                        for (int b = 0; b < 4; ++b) keepb |= (key0 + b < kv_len ? 0xffu : 0u) << (8 * b);
-                        a[i] = (int)((uint32_t)a[i] & keepb);
-                    }
+                    for (int b = 0; b < 4; ++b) m |= (key0 + b < kv_len ? 0xffu : 0u) << (8 * b);
+                    keepb[i] = m;
                 }
-                acc[db] = mfma8(a, pb, acc[db]);
+#pragma unroll
+                for (int db = 0; db < C::DBLK; ++db)
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) va[db][i] = (int)((uint32_t)va[db][i] & keepb[i]);
             }
+#pragma unroll
+            for (int db = 0; db < C::DBLK; ++db) acc[db] = mfma8(va[db], pb, acc[db]);
         }
-        wait_loads8();
-        __syncthreads();
+        wait_older_and_sync<D>();
     };
-    int j = 0;
-    for (; j + 1 < ntiles; j += 2) {
-        step(j, s0, s1);
-        step(j + 1, s1, s0);
+    for (int j = 0; j < ntiles; j += 3) {
+        step(j, s0, s2);
+        if (j + 1 < ntiles) step(j + 1, s1, s0);
+        if (j + 2 < ntiles) step(j + 2, s2, s1);
     }
-    if (j < ntiles) step(j, s0, s1);
 
     // epilogue: O = v_descale · Oᵀ / ℓ -> bf16, LSE
     const float l_tot = pair_sum8(l_run);
