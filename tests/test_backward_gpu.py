@@ -105,3 +105,75 @@ def test_backward_scale_edge_cases(dev, scale):
 def test_backward_medium(dev):
     # several query and key tiles in both kernels, grouped heads, causal
     run_case(dev, 1, 4, 2, 700, 128, True, None, seed=17)
+
+
+def _workload_backward(dev, wid):
+    """Forward + backward of a named workload at full size, in the launch
+    configuration bench.py times (same inputs and seeded dout)."""
+    from workloads import WORKLOADS, make_inputs
+
+    w = WORKLOADS[wid]
+    q, k, v, kl = make_inputs(w)
+    g = torch.Generator().manual_seed(1000 + w.seed)
+    do = torch.randn(q.shape, generator=g).to(torch.bfloat16)
+    qd, kd, vd, dod = q.to(dev), k.to(dev), v.to(dev), do.to(dev)
+    kld = None if kl is None else kl.to(dev)
+    o, lse = attn.forward(qd, kd, vd, scale=w.scale, causal=w.causal, key_lens=kld)
+    dq, dk, dv = attn.backward(qd, kd, vd, o, lse, dod, scale=w.scale, causal=w.causal, key_lens=kld)
+    torch.cuda.synchronize()
+    return w, (q, k, v, do, kl), (dq.cpu(), dk.cpu(), dv.cpu())
+
+
+def _compare(what, got, want):
+    g64 = as_f64(got)
+    assert not np.isnan(g64).any(), f"{what}: NaN"
+    err = float(np.max(np.abs(g64 - want)))
+    mag = float(np.max(np.abs(want)))
+    print(f"  {what}: max err {err:.3e}  max |ref| {mag:.3e}", flush=True)
+    assert err <= TOL_REL * mag + 1e-6, f"{what}: max err {err:.3e} > {TOL_REL} x {mag:.3e}"
+
+
+def test_backward_workload2_full(dev):
+    """Workload 2 (B4 H8 N1024 d64) at full size: every gradient element."""
+    w, (q, k, v, do, kl), grads = _workload_backward(dev, 2)
+    ref = oracle.attention_backward(as_f64(q), as_f64(k), as_f64(v), as_f64(do), w.scale, causal=w.causal)
+    for name, got, want in zip(("dQ", "dK", "dV"), grads, ref):
+        _compare(f"workload 2 {name}", got, want)
+
+
+def test_backward_workload3_heads(dev):
+    """Workload 3 (causal B2 H8 N4096 d64) at full size; two whole heads
+    against the oracle (each head is its own kv head there)."""
+    w, (q, k, v, do, kl), (dq, dk, dv) = _workload_backward(dev, 3)
+    for b, h in ((0, 0), (1, 7)):
+        ref = oracle.attention_backward(as_f64(q[b:b + 1, h:h + 1]), as_f64(k[b:b + 1, h:h + 1]),
+                                        as_f64(v[b:b + 1, h:h + 1]), as_f64(do[b:b + 1, h:h + 1]), w.scale,
+                                        causal=True)
+        for name, got, want in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
+            _compare(f"workload 3 b={b} h={h} {name}", got[b:b + 1, h:h + 1], want)
+
+
+@pytest.mark.parametrize("wid", [4, 5])
+def test_backward_long_workloads_column_sums(dev, wid):
+    """Workloads 4 and 5 at full size (too large for the oracle's N x N
+    matrices): a property of the definition that holds at any size.  Each
+    admissible row's weights sum to one, so for every kv head the dV rows
+    summed over the keys equal the dO rows summed over that head's query
+    heads; padded keys get exactly zero gradients.  Tolerance: the weights
+    are bf16 operands (2^-9 each) and dV is stored in bf16."""
+    w, (q, k, v, do, kl), (dq, dk, dv) = _workload_backward(dev, wid)
+    group = w.H // w.Hkv
+    do64, dv64 = as_f64(do), as_f64(dv)
+    assert not np.isnan(as_f64(dq)).any() and not np.isnan(as_f64(dk)).any() and not np.isnan(dv64).any()
+    for b in range(w.B):
+        n = w.N if kl is None else int(kl[b])
+        if kl is not None:
+            assert np.all(as_f64(dk)[b, :, n:] == 0) and np.all(dv64[b, :, n:] == 0), "padded keys"
+        for g in range(w.Hkv):
+            got = dv64[b, g, :n].sum(axis=0)
+            want = do64[b, g * group:(g + 1) * group].sum(axis=(0, 1))
+            tol = 2.0 ** -8 * np.abs(do64[b, g * group:(g + 1) * group]).sum(axis=(0, 1)) \
+                + 2.0 ** -8 * np.abs(dv64[b, g, :n]).sum(axis=0)
+            worst = float(np.max(np.abs(got - want) / tol))
+            assert worst <= 1.0, f"workload {wid} b={b} g={g}: column sums of dV off by {worst:.2f}x the bound"
+        print(f"  workload {wid} b={b}: dV column sums within bounds", flush=True)
