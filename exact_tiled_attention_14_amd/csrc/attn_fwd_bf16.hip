@@ -55,12 +55,14 @@
 namespace attn {
 namespace {
 
-template <int D>
+// W: waves per wave group (4, or 8 for d = 128 on large grids: 256 query
+// rows share each 128-key tile)
+template <int D, int W>
 struct Cfg;
 
-template <>
-struct Cfg<128> {
-    static constexpr int BC = 64;
+template <int W>
+struct Cfg<128, W> {
+    static constexpr int BC = W == 8 ? 128 : 64;
     static constexpr int KROW = 128 * 2 + 16;  // padded K row (bytes)
     static constexpr int VROW = 128 * 2;       // V row (bytes)
     static constexpr int K_BYTES = BC * KROW;
@@ -73,8 +75,8 @@ struct Cfg<128> {
     }
 };
 
-template <>
-struct Cfg<64> {
+template <int W>
+struct Cfg<64, W> {
     static constexpr int BC = 64;
     static constexpr int KROW = 64 * 2 + 16;
     static constexpr int VROW = 64 * 2;
@@ -86,9 +88,9 @@ struct Cfg<64> {
     }
 };
 
-template <int D>
+template <int D, int W>
 struct Geo {
-    using L = Cfg<D>;
+    using L = Cfg<D, W>;
     static constexpr int BC = L::BC;
     static constexpr int KBLK = BC / 32;   // 32-key MFMA blocks per tile
     static constexpr int DCH = D / 16;     // 16-wide d chunks (Sᵀ k steps)
@@ -96,18 +98,18 @@ struct Geo {
     static constexpr int STAGE = L::K_BYTES + L::V_BYTES;
     static constexpr int NK = L::K_BYTES / 1024;  // 1 KiB direct-load instructions per K tile
     static constexpr int NV = L::V_BYTES / 1024;
-    static constexpr int KI = (NK + kWaves - 1) / kWaves;  // per wave
-    static constexpr int VI = NV / kWaves;
-    static_assert(L::K_BYTES % 1024 == 0 && NV % kWaves == 0, "tiles must split into 1 KiB wave loads");
+    static constexpr int KI = (NK + W - 1) / W;  // per wave
+    static constexpr int VI = NV / W;
+    static_assert(L::K_BYTES % 1024 == 0 && NV % W == 0, "tiles must split into 1 KiB wave loads");
 };
 
 __device__ __forceinline__ int swap23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
 // Per-lane byte offsets, fixed for the whole kernel.
-template <int D>
+template <int D, int W>
 struct Offsets {
-    using G = Geo<D>;
-    using L = Cfg<D>;
+    using G = Geo<D, W>;
+    using L = Cfg<D, W>;
     uint32_t k_src[G::KI];   // global offset (in the tile) of the 16 bytes this lane moves in K load i
     uint32_t v_src[G::VI];
     uint32_t k_rd;           // LDS: Sᵀ A operand, key block 0, d chunk 0
@@ -118,14 +120,14 @@ struct Offsets {
         const int hl = lane >> 5, ql = lane & 31;
 #pragma unroll
         for (int i = 0; i < G::KI; ++i) {
-            const int pos = 1024 * (wave + kWaves * i) + 16 * lane;  // LDS byte in the K tile
+            const int pos = 1024 * (wave + W * i) + 16 * lane;  // LDS byte in the K tile
             const int row = pos / L::KROW, off = pos % L::KROW;
             // the 16 pad bytes of a row take a copy of the row's first chunk
             k_src[i] = (uint32_t)(row * row_bytes + (off < D * 2 ? off : 0));
         }
 #pragma unroll
         for (int i = 0; i < G::VI; ++i) {
-            const int pos = 1024 * (wave + kWaves * i) + 16 * lane;  // LDS byte in the V tile
+            const int pos = 1024 * (wave + W * i) + 16 * lane;  // LDS byte in the V tile
             const int key = pos / L::VROW;
             v_src[i] = (uint32_t)(key * row_bytes + (L::vpos(key, pos % L::VROW) - key * L::VROW));
         }
@@ -146,23 +148,23 @@ typedef __attribute__((address_space(3))) void lds_void;
 // the 1 KiB loads.  The descriptors start at key kv0 and end at the key
 // length (or the tile's end), so rows past the key length are zeros: NaN or
 // any other content there can never reach the output.
-template <int D>
-__device__ __forceinline__ void load_tile(const Offsets<D>& o, char* stage, const uint16_t* kb,
+template <int D, int W>
+__device__ __forceinline__ void load_tile(const Offsets<D, W>& o, char* stage, const uint16_t* kb,
                                           const uint16_t* vb, int kv0, int kv_len, int stride, int wave) {
 #if defined(__HIP_DEVICE_COMPILE__)  // (the LDS-destination builtin does not exist for the host pass)
-    using G = Geo<D>;
+    using G = Geo<D, W>;
     const uint32_t bytes = (uint32_t)min(kv_len - kv0, G::BC) * (uint32_t)(stride * 2);
     const __amdgpu_buffer_rsrc_t kres = make_rsrc(kb + (size_t)kv0 * stride, bytes);
     const __amdgpu_buffer_rsrc_t vres = make_rsrc(vb + (size_t)kv0 * stride, bytes);
 #pragma unroll
     for (int i = 0; i < G::KI; ++i) {
-        const int t = wave + kWaves * i;
+        const int t = wave + W * i;
         if (t < G::NK) __builtin_amdgcn_raw_ptr_buffer_load_lds(kres, (lds_void*)(stage + 1024 * t), 16, o.k_src[i], 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < G::VI; ++i) {
-        const int t = wave + kWaves * i;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vres, (lds_void*)(stage + Cfg<D>::K_BYTES + 1024 * t), 16, o.v_src[i], 0,
+        const int t = wave + W * i;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vres, (lds_void*)(stage + Cfg<D, W>::K_BYTES + 1024 * t), 16, o.v_src[i], 0,
                                                  0, 0);
     }
 #endif
@@ -191,9 +193,9 @@ __device__ __forceinline__ float pair_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D>
+template <int D, int W>
 struct WaveState {
-    f32x16 acc[Geo<D>::DBLK];
+    f32x16 acc[Geo<D, W>::DBLK];
     float m_run;  // reference max, base-2 scaled units (−∞ before the first tile)
     float l_run;  // running sum over this lane's keys
 };
@@ -227,8 +229,8 @@ __device__ __forceinline__ void apply_mask(f32x16& s, int blk, int kv0, int kv_l
 
 // Exact running-max update for one 32-key block (safe_softmax_block): new
 // max, α rescale of ℓ and Oᵀ, P as bf16 pairs.
-template <int D>
-__device__ __forceinline__ void softmax_block_exact(const f32x16& s, uint32_t (&pb)[8], WaveState<D>& w, float c2) {
+template <int D, int W>
+__device__ __forceinline__ void softmax_block_exact(const f32x16& s, uint32_t (&pb)[8], WaveState<D, W>& w, float c2) {
     float mx = kNegInf;
 #pragma unroll
     for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[r], s[r + 1]));
@@ -239,18 +241,18 @@ __device__ __forceinline__ void softmax_block_exact(const f32x16& s, uint32_t (&
     w.m_run = m_new;
     w.l_run = w.l_run * alpha + lsum;
 #pragma unroll
-    for (int i = 0; i < Geo<D>::DBLK; ++i) w.acc[i] *= alpha;
+    for (int i = 0; i < Geo<D, W>::DBLK; ++i) w.acc[i] *= alpha;
 }
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
-template <int D>
-__device__ __forceinline__ void pv_block(WaveState<D>& w, const char* vs, const Offsets<D>& o, int blk,
+template <int D, int W>
+__device__ __forceinline__ void pv_block(WaveState<D, W>& w, const char* vs, const Offsets<D, W>& o, int blk,
                                          const uint32_t (&pb)[8]) {
-    constexpr int VROW = Cfg<D>::VROW;
+    constexpr int VROW = Cfg<D, W>::VROW;
 #pragma unroll
-    for (int db = 0; db < Geo<D>::DBLK; ++db)
+    for (int db = 0; db < Geo<D, W>::DBLK; ++db)
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
             const char* at = vs + o.v_rd[db] + (32 * blk + 16 * c) * VROW;
@@ -262,22 +264,22 @@ __device__ __forceinline__ void pv_block(WaveState<D>& w, const char* vs, const 
         }
 }
 
-template <int D>
-__device__ __forceinline__ void qk_block(f32x16& s, const char* ks, const Offsets<D>& o,
-                                         const bf16x8 (&qf)[Geo<D>::DCH], int blk) {
+template <int D, int W>
+__device__ __forceinline__ void qk_block(f32x16& s, const char* ks, const Offsets<D, W>& o,
+                                         const bf16x8 (&qf)[Geo<D, W>::DCH], int blk) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.f;
-    uint4 a[Geo<D>::DCH];
+    uint4 a[Geo<D, W>::DCH];
 #pragma unroll
-    for (int c = 0; c < Geo<D>::DCH; ++c) a[c] = *reinterpret_cast<const uint4*>(ks + o.k_rd + blk * 32 * Cfg<D>::KROW + c * 32);
+    for (int c = 0; c < Geo<D, W>::DCH; ++c) a[c] = *reinterpret_cast<const uint4*>(ks + o.k_rd + blk * 32 * Cfg<D, W>::KROW + c * 32);
 #pragma unroll
-    for (int c = 0; c < Geo<D>::DCH; ++c)
+    for (int c = 0; c < Geo<D, W>::DCH; ++c)
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[c]), qf[c], s, 0, 0, 0);
     if (blk == 0) {
         // a tile's first block has no other work to hide the LDS latency
         // behind: issue all its operand reads before its MFMAs
-        __builtin_amdgcn_sched_group_barrier(0x100, Geo<D>::DCH, 0);  // LDS reads
-        __builtin_amdgcn_sched_group_barrier(0x008, Geo<D>::DCH, 0);  // MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, Geo<D, W>::DCH, 0);  // LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, Geo<D, W>::DCH, 0);  // MFMAs
     }
 }
 
@@ -291,23 +293,23 @@ __device__ __forceinline__ void qk_block(f32x16& s, const char* ks, const Offset
 // (Oᵀ and ℓ are still zero there); MODE 2: exact running-max update on every
 // block (its α rescale of Oᵀ follows the previous block's Oᵀ MFMAs and
 // precedes this block's).
-template <int D, bool CAUSAL, int MODE>
-__device__ __forceinline__ void tile(WaveState<D>& w, const char* stage, const Offsets<D>& o,
-                                     const bf16x8 (&qf)[Geo<D>::DCH], float c2, bool masked, int kv0,
+template <int D, int W, bool CAUSAL, int MODE>
+__device__ __forceinline__ void tile(WaveState<D, W>& w, const char* stage, const Offsets<D, W>& o,
+                                     const bf16x8 (&qf)[Geo<D, W>::DCH], float c2, bool masked, int kv0,
                                      int kv_len, int qrow, int hl, bool first) {
-    constexpr int KBLK = Geo<D>::KBLK;
+    constexpr int KBLK = Geo<D, W>::KBLK;
     f32x16 s[2];
     uint32_t pb[2][8];
-    qk_block<D>(s[0], stage, o, qf, 0);
-    const char* vs = stage + Cfg<D>::K_BYTES;
+    qk_block<D, W>(s[0], stage, o, qf, 0);
+    const char* vs = stage + Cfg<D, W>::K_BYTES;
 #pragma unroll
     for (int blk = 0; blk < KBLK; ++blk) {
-        if (blk + 1 < KBLK) qk_block<D>(s[(blk + 1) & 1], stage, o, qf, blk + 1);
-        if (blk > 0) pv_block<D>(w, vs, o, blk - 1, pb[(blk - 1) & 1]);
+        if (blk + 1 < KBLK) qk_block<D, W>(s[(blk + 1) & 1], stage, o, qf, blk + 1);
+        if (blk > 0) pv_block<D, W>(w, vs, o, blk - 1, pb[(blk - 1) & 1]);
         f32x16& sb = s[blk & 1];
         if (MODE != 1 && masked) apply_mask<CAUSAL>(sb, blk, kv0, kv_len, qrow, hl);
         if (MODE == 2) {
-            softmax_block_exact<D>(sb, pb[blk & 1], w, c2);
+            softmax_block_exact<D, W>(sb, pb[blk & 1], w, c2);
         } else {
             if (MODE == 3 && blk == 0 && first) {
                 float mx = kNegInf;
@@ -320,12 +322,12 @@ __device__ __forceinline__ void tile(WaveState<D>& w, const char* stage, const O
         }
         if (MODE == 1) __builtin_amdgcn_sched_barrier(0);  // keep the block pipeline order
     }
-    pv_block<D>(w, vs, o, KBLK - 1, pb[(KBLK - 1) & 1]);
+    pv_block<D, W>(w, vs, o, KBLK - 1, pb[(KBLK - 1) & 1]);
 }
 
 // LDS stages: two separate __shared__ objects of KSPLIT stages each; group g
 // double-buffers in (s0 + g·STAGE, s1 + g·STAGE).
-template <int D, int KSPLIT>
+template <int D, int W, int KSPLIT>
 struct Lds {
     char* s0;
     char* s1;
@@ -337,19 +339,20 @@ struct Lds {
 // disjoint key sets are combined by the softmax-merge rule (unite.ai page,
 // section "闪电注意力的数学原理", formula 2): m = max(m0, m1), each side scaled
 // by 2^(m_g − m).  It doubles the waves per SIMD when the grid alone cannot.
-template <int D, bool CAUSAL, int KSPLIT, bool GEN>
-__device__ __forceinline__ void attend_tile(const Params& p, const Tile& t, const Lds<D, KSPLIT>& lds) {
-    using G = Geo<D>;
+template <int D, int W, bool CAUSAL, int KSPLIT, bool GEN>
+__device__ __forceinline__ void attend_tile(const Params& p, const Tile& t, const Lds<D, W, KSPLIT>& lds) {
+    using G = Geo<D, W>;
     constexpr int BC = G::BC;
 
-    const int tid = threadIdx.x % kThreads;  // thread index within the group
+    constexpr int BR = 32 * W;  // query rows of the workgroup
+    const int tid = threadIdx.x % (64 * W);  // thread index within the group
     const int wave_all = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-    const int grp = wave_all / kWaves;       // key-split group
-    const int wave = wave_all % kWaves;      // wave within the group
+    const int grp = wave_all / W;            // key-split group
+    const int wave = wave_all % W;           // wave within the group
     const int lane = tid & 63;
     const int hl = lane >> 5, ql = lane & 31;
 
-    const int q0 = t.tile * kBR;
+    const int q0 = t.tile * BR;
     const int q0w = q0 + wave * 32;
     const int qrow = q0w + ql;
     const int g = t.h / (p.H / p.Hkv);
@@ -360,7 +363,7 @@ __device__ __forceinline__ void attend_tile(const Params& p, const Tile& t, cons
     const int dq = GEN ? R.delta : 0;  // causal: key j admissible for row i iff j <= i + dq
     // keys this workgroup looks at: the admissible ones, cut under a causal
     // mask at the tile's last query row
-    const int kv_hi = CAUSAL ? min(kv_len, max(min(q0 + kBR, R.n_q) + dq, 0)) : kv_len;
+    const int kv_hi = CAUSAL ? min(kv_len, max(min(q0 + BR, R.n_q) + dq, 0)) : kv_len;
     const int ntiles = (kv_hi + BC - 1) / BC;
     const int niters = (ntiles + KSPLIT - 1) / KSPLIT;  // tile it = KSPLIT·j + grp
     const int ks = R.kv_stride;
@@ -382,13 +385,13 @@ __device__ __forceinline__ void attend_tile(const Params& p, const Tile& t, cons
     uint32_t flip = p.negate_q ? 0x80008000u : 0u;
     uint32_t keep = p.zero_q ? 0u : 0xffffffffu;
 
-    Offsets<D> o;
+    Offsets<D, W> o;
     o.init(wave, lane, ks * 2);
     // this group's two stages (in distinct LDS objects; see Lds)
     char* const S0 = lds.s0 + grp * G::STAGE;
     char* const S1 = lds.s1 + grp * G::STAGE;
 
-    WaveState<D> w;
+    WaveState<D, W> w;
     const float c2 = p.scale_log2;
     // First a fast pass; if any row of the workgroup overflowed, an exact pass.
     for (bool exact_all = false;; exact_all = true) {
@@ -399,7 +402,7 @@ __device__ __forceinline__ void attend_tile(const Params& p, const Tile& t, cons
         w.m_run = kNegInf;
         w.l_run = 0.f;
 
-        if (grp < ntiles) load_tile<D>(o, S0, kb, vb, grp * BC, kv_len, ks, wave);
+        if (grp < ntiles) load_tile<D, W>(o, S0, kb, vb, grp * BC, kv_len, ks, wave);
         // (identity on the exact pass: flip and keep are reset below)
         bf16x8 qf[G::DCH];
 #pragma unroll
@@ -422,13 +425,13 @@ __device__ __forceinline__ void attend_tile(const Params& p, const Tile& t, cons
             constexpr int MODE = decltype(mode_tag)::value;
             const int it = KSPLIT * j + grp;
             const int kv0 = it * BC;
-            if (it + KSPLIT < ntiles) load_tile<D>(o, next, kb, vb, kv0 + KSPLIT * BC, kv_len, ks, wave);
+            if (it + KSPLIT < ntiles) load_tile<D, W>(o, next, kb, vb, kv0 + KSPLIT * BC, kv_len, ks, wave);
             if (MODE == 1) {
-                tile<D, CAUSAL, 1>(w, cur, o, qf, c2, false, kv0, kv_len, qrow, hl, false);
+                tile<D, W, CAUSAL, 1>(w, cur, o, qf, c2, false, kv0, kv_len, qrow, hl, false);
             } else if (it < ntiles && !(CAUSAL && kv0 > q0w + 31 + dq)) {
                 // (under a causal mask a wave whose rows all precede the tile skips it)
                 const bool masked = (kv0 + BC > kv_len) || (CAUSAL && kv0 + BC - 1 > q0w + dq);
-                tile<D, CAUSAL, MODE>(w, cur, o, qf, c2, masked, kv0, kv_len, qrow + dq, hl, j == 0);
+                tile<D, W, CAUSAL, MODE>(w, cur, o, qf, c2, masked, kv0, kv_len, qrow + dq, hl, j == 0);
             }
             wait_loads();
             __syncthreads();
@@ -478,7 +481,7 @@ __device__ __forceinline__ void attend_tile(const Params& p, const Tile& t, cons
     if (KSPLIT == 2) {
         // merge group 1's partial result into group 0 (lane-contiguous LDS rows)
         constexpr int NV = G::DBLK * 16 + 2;
-        static_assert(KSPLIT == 1 || kWaves * NV * 64 * 4 <= KSPLIT * G::STAGE, "the merge rows must fit in s0");
+        static_assert(KSPLIT == 1 || W * NV * 64 * 4 <= KSPLIT * G::STAGE, "the merge rows must fit in s0");
         float* xch = reinterpret_cast<float*>(lds.s0) + (wave * NV) * 64 + lane;
         __syncthreads();  // every group is done with its LDS stages
         if (grp == 1) {
@@ -579,43 +582,54 @@ __device__ __forceinline__ bool persistent_item(const Params& p, int i, Tile* t)
 // GEN: the general form (packed sequences, key ranges of their own or split,
 // a causal diagonal offset, fp32 partial output); the plain form reads none
 // of those fields.
-template <int D, bool CAUSAL, int KSPLIT, bool PERSIST, bool GEN>
-__global__ __launch_bounds__(kThreads * KSPLIT, KSPLIT == 1 ? (D == 64 ? 3 : 2) : 1) void attn_fwd_bf16_kernel(Params p) {
-    __shared__ __attribute__((aligned(16))) char s0[KSPLIT * Geo<D>::STAGE];
-    __shared__ __attribute__((aligned(16))) char s1[KSPLIT * Geo<D>::STAGE];
-    const Lds<D, KSPLIT> lds{s0, s1};
+template <int D, int W, bool CAUSAL, int KSPLIT, bool PERSIST, bool GEN>
+__global__ __launch_bounds__(64 * W * KSPLIT, (KSPLIT == 1 && W == 4) ? (D == 64 ? 3 : 2) : 1) void attn_fwd_bf16_kernel(
+    Params p) {
+    __shared__ __attribute__((aligned(16))) char s0[KSPLIT * Geo<D, W>::STAGE];
+    __shared__ __attribute__((aligned(16))) char s1[KSPLIT * Geo<D, W>::STAGE];
+    const Lds<D, W, KSPLIT> lds{s0, s1};
     if (!PERSIST) {
-        attend_tile<D, CAUSAL, KSPLIT, GEN>(p, map_workgroup<CAUSAL, GEN>(p), lds);
+        attend_tile<D, W, CAUSAL, KSPLIT, GEN>(p, map_workgroup<CAUSAL, GEN>(p), lds);
         return;
     }
     Tile t;
     for (int i = 0; persistent_item<GEN>(p, i, &t); ++i) {
         if (i > 0) __syncthreads();  // the previous item's LDS traffic is done
-        attend_tile<D, CAUSAL, KSPLIT, GEN>(p, t, lds);
+        attend_tile<D, W, CAUSAL, KSPLIT, GEN>(p, t, lds);
     }
 }
 
 template <int D, bool CAUSAL, bool GEN>
 void launch_g(const Params& p, const Schedule& sc, hipStream_t stream) {
     const dim3 grid((unsigned)sc.grid);
+    constexpr int T = 64 * 4;  // threads per 4-wave group
     if (sc.ksplit == 2) {
         if (sc.persistent)
-            hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, 2, true, GEN>), grid, dim3(2 * kThreads), 0, stream, p);
+            hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, 4, CAUSAL, 2, true, GEN>), grid, dim3(2 * T), 0, stream, p);
         else
-            hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, 2, false, GEN>), grid, dim3(2 * kThreads), 0, stream, p);
+            hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, 4, CAUSAL, 2, false, GEN>), grid, dim3(2 * T), 0, stream, p);
     } else {
         if (sc.persistent)
-            hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, 1, true, GEN>), grid, dim3(kThreads), 0, stream, p);
+            hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, 4, CAUSAL, 1, true, GEN>), grid, dim3(T), 0, stream, p);
         else
-            hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, CAUSAL, 1, false, GEN>), grid, dim3(kThreads), 0, stream, p);
+            hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, 4, CAUSAL, 1, false, GEN>), grid, dim3(T), 0, stream, p);
     }
 }
 
 template <int D, bool CAUSAL>
 void launch_d(const Params& p, const Schedule& sc, hipStream_t stream) {
     const bool gen = p.cu_seqlens != nullptr || p.splits > 1 || p.o_f32 != nullptr || p.delta != 0 || p.Nk != p.N;
-    if (gen) launch_g<D, CAUSAL, true>(p, sc, stream);
-    else launch_g<D, CAUSAL, false>(p, sc, stream);
+    if (gen) {
+        launch_g<D, CAUSAL, true>(p, sc, stream);
+    } else if (D == 128 && sc.ksplit == 1 && !sc.persistent) {
+        // large d = 128 grids: eight waves (256 query rows) per 128-key tile
+        Params p8 = p;
+        p8.q_tiles = (p.N + 255) / 256;
+        const dim3 grid((unsigned)(p.B * p.H * p8.q_tiles));
+        hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, 8, CAUSAL, 1, false, false>), grid, dim3(64 * 8), 0, stream, p8);
+    } else {
+        launch_g<D, CAUSAL, false>(p, sc, stream);
+    }
 }
 
 }  // namespace

@@ -63,6 +63,9 @@ SMALL = [  # (B, H, Hkv, N, d): several tiles, ragged tails, grouped heads
     (4, 64, 16, 260, 64), (2, 128, 32, 300, 128),
     # enough causal query tiles per CU for the non-persistent causal schedule
     (8, 64, 16, 300, 64),
+    # d = 128 on a large grid: the eight-wave (256-row) workgroups, ragged
+    # in the last query tile, causal and not
+    (8, 64, 16, 300, 128),
 ]
 
 
