@@ -1,10 +1,11 @@
-// attn_common.h — device helpers shared by the bf16 and fp32 forward kernels.
+// attn_common.h — device helpers shared by the attention kernels.
 //
 // Work decomposition (the query-block-outer, key-block-inner loop of the
 // tiled forward pass: zsdodo.com page "AI训练的最大障碍不是算力,而是“内存墙”",
 // blockwise code block; aiknowledge.cn "第四章 注意力机制实战案例" §4.1.3): one
-// workgroup owns BR = 128 query rows of one (batch, head); each of its four
-// 64-wide waves owns 32 of those rows.
+// workgroup owns a tile of query rows of one (batch, head), kBR = 128 rows of
+// four 64-wide waves that own 32 rows each (the bf16 forward also has an
+// eight-wave, 256-row form for d = 128 on large grids).
 #pragma once
 
 #include <hip/hip_runtime.h>

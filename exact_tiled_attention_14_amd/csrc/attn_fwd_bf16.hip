@@ -1,9 +1,9 @@
 // attn_fwd_bf16.hip — exact tiled attention forward, bf16 storage, gfx950.
 //
-// One workgroup = 4 waves = BR = 128 query rows of one (b, h).  Each wave holds
-// its 32 query rows in registers for the whole kernel and streams the head's
-// K/V in tiles of BC keys (BC·d = 8192 elements, 16 KiB per tile of K and of
-// V) through a double-buffered LDS stage.  Per tile and wave:
+// One workgroup = W waves (4, or 8 for d = 128 on large grids) = 32·W query
+// rows of one (b, h).  Each wave holds its 32 query rows in registers for the
+// whole kernel and streams the head's K/V in tiles of BC keys (64, or 128 with
+// 8 waves) through a double-buffered LDS stage.  Per tile and wave:
 //
 //   Sᵀ = K_tile · Qᵀ            v_mfma_f32_32x32x16_bf16, fp32 accumulate
 //   mask (only on tiles that straddle the causal diagonal or the key end)
