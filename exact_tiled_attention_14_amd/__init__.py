@@ -49,6 +49,7 @@ ENTRY_POINTS = {
     "attn_fwd_fp8": ([_P] * 5 + [ctypes.c_float] * 3 + [_I] * 5 + [ctypes.c_float, _I, _P, _P], ctypes.c_int),
     "attn_bwd_bf16": ([_P] * 10 + [_I, _I, _I, _I, _I, ctypes.c_float, _I, _P, _P], ctypes.c_int),
     "attn_status_str": ([_I], ctypes.c_char_p),
+    "attn_last_hip_error": ([], ctypes.c_char_p),
 }
 
 
@@ -57,7 +58,10 @@ class AttnError(RuntimeError):
 
     def __init__(self, status, where):
         self.status = status
-        super().__init__(f"{where}: status {status} ({attn_status_str(status)})")
+        text = f"{where}: status {status} ({attn_status_str(status)})"
+        if status == ATTN_ERR_HIP:
+            text += ": " + load_library().attn_last_hip_error().decode()
+        super().__init__(text)
 
 
 def library_path():
@@ -73,6 +77,13 @@ def load_library():
             raise RuntimeError(
                 f"{path} is missing: build it first (python -m exact_tiled_attention_14_amd.build); "
                 "there is no fallback implementation")
+        # PyTorch-ROCm carries its own HIP and HSA runtimes under the same
+        # sonames as /opt/rocm's.  Loaded first, they satisfy the library's
+        # libamdhip64.so.7 dependency and the process has one runtime; loaded
+        # after the library, a second pair comes in beside it, and the
+        # library's runtime then finds no device (hipErrorNoDevice).
+        import torch  # noqa: F401
+
         lib = ctypes.CDLL(path)
         for name, (argtypes, restype) in ENTRY_POINTS.items():
             fn = getattr(lib, name)

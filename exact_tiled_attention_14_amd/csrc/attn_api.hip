@@ -3,6 +3,7 @@
 #include <float.h>
 #include <math.h>
 #include <stdint.h>
+#include <stdio.h>
 
 #include "attn.h"
 #include "attn_common.h"
@@ -66,6 +67,15 @@ int validate(const void* q, const void* k, const void* v, const void* o, const v
     return ATTN_OK;
 }
 
+// The HIP error behind the calling thread's latest ATTN_ERR_HIP.
+thread_local hipError_t last_hip_error = hipSuccess;
+
+int hip_status(hipError_t e) {
+    if (e == hipSuccess) return ATTN_OK;
+    last_hip_error = e;
+    return ATTN_ERR_HIP;
+}
+
 // Number of compute units of the current device (cached per device).
 int device_cus() {
     static int cached[64] = {0};
@@ -117,7 +127,7 @@ int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* l
     (void)hipGetLastError();
     const hipError_t e =
         attn::launch_fwd_bf16(p, d, causal != 0, schedule_bf16(p, causal != 0), static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+    return hip_status(e);
 }
 
 int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
@@ -129,7 +139,7 @@ int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float
     if (st != ATTN_OK || empty) return st;
     (void)hipGetLastError();
     const hipError_t e = attn::launch_fwd_f32(p, d, causal != 0, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+    return hip_status(e);
 }
 
 int attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
@@ -152,7 +162,7 @@ int attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o, co
     bp.scale = scale;
     (void)hipGetLastError();
     const hipError_t e = attn::launch_bwd_bf16(bp, d, causal != 0, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+    return hip_status(e);
 }
 
 int attn_fwd_varlen_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -177,7 +187,7 @@ int attn_fwd_varlen_bf16(const void* q, const void* k, const void* v, void* o, f
     (void)hipGetLastError();
     const hipError_t e =
         attn::launch_fwd_bf16(p, d, causal != 0, schedule_bf16(p, causal != 0), static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+    return hip_status(e);
 }
 
 int attn_fwd_partial_bf16(const void* q, const void* k, const void* v, float* o_part, float* lse_part,
@@ -205,7 +215,7 @@ int attn_fwd_partial_bf16(const void* q, const void* k, const void* v, float* o_
     (void)hipGetLastError();
     const hipError_t e =
         attn::launch_fwd_bf16(p, d, causal != 0, schedule_bf16(p, causal != 0), static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+    return hip_status(e);
 }
 
 int attn_merge(const float* o_parts, const float* lse_parts, int S, int B, int H, int N, int d,
@@ -220,7 +230,7 @@ int attn_merge(const float* o_parts, const float* lse_parts, int S, int B, int H
     (void)hipGetLastError();
     const hipError_t e = attn::launch_merge(o_parts, lse_parts, S, (int64_t)B * H * N, d, o, o_bf16 != 0, lse,
                                             static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+    return hip_status(e);
 }
 
 namespace {
@@ -262,7 +272,7 @@ int attn_fwd_splitkv_bf16(const void* q, const void* k, const void* v, void* o, 
     (void)hipGetLastError();
     if (S == 1) {  // one range: the plain forward pass
         const hipError_t e = attn::launch_fwd_bf16(p, d, causal != 0, schedule_bf16(p, causal != 0), hs);
-        return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+        return hip_status(e);
     }
     const size_t need = attn_splitkv_workspace_bytes(B, H, Nq, d, num_splits);
     if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
@@ -275,9 +285,9 @@ int attn_fwd_splitkv_bf16(const void* q, const void* k, const void* v, void* o, 
     p.o_f32 = o_parts;
     p.lse = lse_parts;
     hipError_t e = attn::launch_fwd_bf16(p, d, causal != 0, schedule_bf16(p, causal != 0), hs);
-    if (e != hipSuccess) return ATTN_ERR_HIP;
+    if (e != hipSuccess) return hip_status(e);
     e = attn::launch_merge(o_parts, lse_parts, S, (int64_t)B * H * Nq, d, o, true, lse, hs);
-    return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+    return hip_status(e);
 }
 
 int attn_fwd_fp8(const void* q, const void* k, const void* vt, void* o, float* lse,
@@ -296,13 +306,21 @@ int attn_fwd_fp8(const void* q, const void* k, const void* vt, void* o, float* l
     p.o_scale = v_descale;
     (void)hipGetLastError();
     const hipError_t e = attn::launch_fwd_fp8(p, d, causal != 0, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+    return hip_status(e);
 }
 
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int H, int Hkv, int N, int d, float scale, int causal,
              const int32_t* key_lens, void* stream) {
     return attn_fwd_bf16(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, key_lens, stream);
+}
+
+const char* attn_last_hip_error(void) {
+    static thread_local char text[256];
+    if (last_hip_error == hipSuccess) return "none";
+    snprintf(text, sizeof(text), "%s (%d): %s", hipGetErrorName(last_hip_error), (int)last_hip_error,
+             hipGetErrorString(last_hip_error));
+    return text;
 }
 
 const char* attn_status_str(int status) {

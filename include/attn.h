@@ -199,6 +199,11 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* attn_status_str(int status);
 
+/* Name, code and text of the HIP error behind the calling thread's most recent
+ * ATTN_ERR_HIP ("none" if it has had none).  The pointer is owned by the
+ * library and stays valid until the thread's next call of this function. */
+const char* attn_last_hip_error(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -7,6 +7,8 @@ import glob
 import math
 import os
 import re
+import subprocess
+import sys
 
 import pytest
 
@@ -103,6 +105,18 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(attn, "library_path", lambda: str(tmp_path / "nope.so"))
     with pytest.raises(RuntimeError, match="no fallback"):
         attn.load_library()
+
+
+def test_one_hip_runtime_whatever_the_import_order():
+    """Loading the library before torch must not bring a second HIP runtime
+    into the process (torch ships its own under the same soname; a second
+    one sees no device).  Checked in a fresh interpreter."""
+    code = ("import exact_tiled_attention_14_amd as a; a.load_library(); import torch; "
+            "print(sorted({l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}))")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr[-2000:]
+    runtimes = eval(out.stdout.strip().splitlines()[-1])
+    assert len(runtimes) == 1, runtimes
 
 
 BWD_GOOD = dict(q=P, k=P * 2, v=P * 3, o=P * 4, dout=P * 5, lse=P * 6, dq=P * 7, dk=P * 8, dv=P * 9,
