@@ -214,6 +214,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdParams p) {
             load_rows<D>(next + G::T_ALLOC, vb, kv0 + G::TILE, kv_len, src, wave);
         }
         if (!(CAUSAL && kv0 > q0w + 31)) {  // a wave whose rows all precede the tile skips it
+            // masks only where the tile passes the key length or (causal) this wave's diagonal
+            const bool masked = (kv0 + G::TILE > kv_len) || (CAUSAL && kv0 + G::TILE - 1 > q0w);
             const char* ks = cur;
             const char* vs = cur + G::T_ALLOC;
 #pragma unroll
@@ -229,14 +231,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdParams p) {
                     dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, b), dof[c], dp, 0, 0, 0);
                 }
                 uint32_t dsb[8];
+                // register r holds key kv0 + 32·blk + 8·hl + 16(r / 8) + r % 8;
+                // admissible iff that constant offset is at most lim
+                const int lim = (CAUSAL ? min(kv_len - 1, qrow) : kv_len - 1) - (kv0 + blk * 32 + 8 * hl);
 #pragma unroll
                 for (int r = 0; r < 16; r += 2) {
                     float e[2];
 #pragma unroll
                     for (int u = 0; u < 2; ++u) {
-                        const int key = kv0 + blk * 32 + 16 * ((r + u) >> 3) + 8 * hl + ((r + u) & 7);
-                        const bool ok = key < kv_len && (!CAUSAL || key <= qrow);
-                        const float pr = ok ? exp2_fast(__builtin_fmaf(s[r + u], c2, -L2)) : 0.f;
+                        float pr = exp2_fast(__builtin_fmaf(s[r + u], c2, -L2));
+                        if (masked) pr = (16 * ((r + u) >> 3) + ((r + u) & 7) <= lim) ? pr : 0.f;
                         e[u] = pr * (dp[r + u] - Drow);
                     }
                     dsb[r >> 1] = pack2(e[0], e[1]);
@@ -399,6 +403,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkv_kernel(BwdParams p) 
                 // register r of half h: query r0 + 32 qb + 16 (r / 8) + 8h + r % 8;
                 // every row with a key here has a finite LSE (key 0 is admissible)
                 uint32_t pb[8], dsb[8];
+                // register r holds query base + 16(r / 8) + r % 8 with base =
+                // r0 + 32·qb + 8·hl; admissible iff that constant offset lies in
+                // [lo, hi] (q < N, key < key length, and key <= q if causal)
+                const int qbase = r0 + qb * 32 + 8 * hl;
+                const int hi = key < kv_len ? N - 1 - qbase : -1;
+                const int lo = CAUSAL ? key - qbase : 0;
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
                     const float4* lp = reinterpret_cast<const float4*>(lse_s + qb * 32 + 16 * hh + 8 * hl);
@@ -414,9 +424,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkv_kernel(BwdParams p) 
                             const int r = 8 * hh + u + w2;
                             float pr = exp2_fast(__builtin_fmaf(s[r], c2, -lv[u + w2] * kLog2e));
                             if (masked) {
-                                const int q = r0 + qb * 32 + 16 * hh + 8 * hl + u + w2;
-                                const bool ok = q < N && key < kv_len && (!CAUSAL || key <= q);
-                                pr = ok ? pr : 0.f;
+                                const int off = 16 * hh + u + w2;
+                                pr = (off >= lo && off <= hi) ? pr : 0.f;
                             }
                             pe[w2] = pr;
                             de[w2] = pr * (dp[r] - dv8[u + w2]);

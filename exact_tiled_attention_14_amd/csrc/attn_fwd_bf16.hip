@@ -216,15 +216,26 @@ __device__ __forceinline__ float exponentiate(const f32x16& s, uint32_t (&pb)[8]
 }
 
 // Inadmissible keys of 32-key block `blk` (past the valid key length, or
-// after the query row under a causal mask) get score −∞.
-template <bool CAUSAL>
+// after the query row under a causal mask) get score −∞.  Register r holds
+// key base + 16(r / 8) + r % 8 with base = kv0 + 32·blk + 8·hl, so both
+// conditions fold into one per-lane limit on that constant offset: one
+// compare and one select per score.  (The eight-wave form keeps the per-key
+// test: the limit form's register allocation spills there.)
+template <bool CAUSAL, int W>
 __device__ __forceinline__ void apply_mask(f32x16& s, int blk, int kv0, int kv_len, int qrow, int hl) {
+    if (W == 8) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int key = kv0 + blk * 32 + 16 * (r >> 3) + 8 * hl + (r & 7);
-        const bool ok = key < kv_len && (!CAUSAL || key <= qrow);
-        s[r] = ok ? s[r] : kNegInf;
+        for (int r = 0; r < 16; ++r) {
+            const int key = kv0 + blk * 32 + 16 * (r >> 3) + 8 * hl + (r & 7);
+            const bool ok = key < kv_len && (!CAUSAL || key <= qrow);
+            s[r] = ok ? s[r] : kNegInf;
+        }
+        return;
     }
+    const int base = kv0 + blk * 32 + 8 * hl;
+    const int lim = (CAUSAL ? min(kv_len - 1, qrow) : kv_len - 1) - base;  // admissible iff offset <= lim
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = (16 * (r >> 3) + (r & 7) <= lim) ? s[r] : kNegInf;
 }
 
 // Exact running-max update for one 32-key block (safe_softmax_block): new
@@ -307,7 +318,7 @@ __device__ __forceinline__ void tile(WaveState<D, W>& w, const char* stage, cons
         if (blk + 1 < KBLK) qk_block<D, W>(s[(blk + 1) & 1], stage, o, qf, blk + 1);
         if (blk > 0) pv_block<D, W>(w, vs, o, blk - 1, pb[(blk - 1) & 1]);
         f32x16& sb = s[blk & 1];
-        if (MODE != 1 && masked) apply_mask<CAUSAL>(sb, blk, kv0, kv_len, qrow, hl);
+        if (MODE != 1 && masked) apply_mask<CAUSAL, W>(sb, blk, kv0, kv_len, qrow, hl);
         if (MODE == 2) {
             softmax_block_exact<D, W>(sb, pb[blk & 1], w, c2);
         } else {

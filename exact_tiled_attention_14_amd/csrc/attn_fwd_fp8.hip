@@ -239,14 +239,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_fp8_kernel(Params p) {
                 for (int c = 0; c < C::DC; ++c) s[blk] = mfma8(read32(cur + o.k_rd[blk] + 64 * c), qf[c], s[blk]);
             }
             if (masked) {
+                // register r of block blk holds key kv0 + 32·hl + 16·blk + r:
+                // one per-lane limit on the constant part, one compare and one
+                // select per score
+                const int lim = (CAUSAL ? min(kv_len - 1, qrow) : kv_len - 1) - (kv0 + 32 * hl);
 #pragma unroll
                 for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = kv0 + 32 * hl + 16 * blk + r;
-                        const bool ok = key < kv_len && (!CAUSAL || key <= qrow);
-                        s[blk][r] = ok ? s[blk][r] : kNegInf;
-                    }
+                    for (int r = 0; r < 16; ++r) s[blk][r] = (16 * blk + r <= lim) ? s[blk][r] : kNegInf;
             }
             // the tile's row max, and the lazy rescale: only when it is more
             // than 2x (base 2: more than 1) above the reference.  Both blocks
