@@ -82,6 +82,22 @@ def stored_traffic(workload_id):
     return None if ent is None else ent.get("bytes_per_launch")
 
 
+def stored_mfma_util(workload_id):
+    """Matrix-core busy fraction and effective shader clock of the forward
+    kernel from the committed rocprofv3 counter runs (SQ_VALU_MFMA_BUSY_CYCLES,
+    SQ_BUSY_CYCLES), or None when absent or taken on another kernel version."""
+    path = os.path.join(ROOT, "profiles", "mfma_util.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    ent = rec.get("workloads", {}).get(str(workload_id))
+    return None if ent is None else {"mfma_busy": ent["mfma_busy"], "clock_ghz": ent["clock_ghz"]}
+
+
 class Runner:
     """Inputs of one workload resident on the GPU and a raw C-ABI launch."""
 
@@ -353,7 +369,8 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
                      "algorithmic_bytes": algorithmic_bytes(w),
-                     "algorithmic_flops": alg},
+                     "algorithmic_flops": alg,
+                     "counters": stored_mfma_util(args.workload)},
     }
 
     if not args.no_extra:
@@ -372,6 +389,7 @@ def main():
                 "algorithmic_tflops": round(a / (m * 1e-3) / 1e12, 2),
                 "frac_of_bf16_peak": round(a / (m * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                 "traffic": stored_traffic(wid),
+                "counters": stored_mfma_util(wid),
             }
             del rr
         line["workloads"] = extra
