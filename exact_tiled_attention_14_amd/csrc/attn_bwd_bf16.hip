@@ -11,14 +11,15 @@
 //
 // (the chain rule through the definition; grouped query heads add their dK
 // and dV into their kv head).  Two kernels, both on v_mfma_f32_32x32x16_bf16
-// with fp32 accumulation, P and dS rounded to bf16 as MFMA operands:
+// with fp32 accumulation, P and dS rounded to bf16 as MFMA operands.
+// attn_bwd_delta_kernel first writes D_i (the `delta` buffer); then one
+// launch of attn_bwd_kernel runs both gradient parts side by side:
 //
-// * attn_bwd_dq_kernel — query-major, the forward kernel's layout: a wave owns
+// * dQ workgroups — query-major, the forward kernel's layout: a wave owns
 //   32 query rows (Q and dO rows in registers as B operands) and streams K/V
 //   tiles of 64 keys through LDS: Sᵀ = K·Qᵀ, dPᵀ = V·dOᵀ, dSᵀ, then
-//   dQᵀ += Kᵀ·dSᵀ with Kᵀ read through ds_read_b64_tr_b16.  It also writes
-//   D_i (the `delta` buffer) for the second kernel.
-// * attn_bwd_dkv_kernel — key-major: a wave owns 32 keys (K and V rows in
+//   dQᵀ += Kᵀ·dSᵀ with Kᵀ read through ds_read_b64_tr_b16.
+// * dK/dV workgroups — key-major: a wave owns 32 keys (K and V rows in
 //   registers as B operands) and streams, for every query head of the kv
 //   head's group, Q/dO tiles of 64 rows (with their LSE and D) through LDS:
 //   S = Q·Kᵀ, dP = dO·Vᵀ, dS, then dVᵀ += dOᵀ·P and dKᵀ += Qᵀ·dS with dOᵀ
@@ -31,6 +32,8 @@
 // reads operand row swap23(lane % 32) (bits 2 and 3 exchanged) so that the
 // MFMA output registers 8c .. 8c + 7 of a half-wave cover 8 consecutive
 // rows, which is the B-operand order of the second product.
+#include <algorithm>
+
 #include "attn_common.h"
 
 namespace attn {
@@ -61,10 +64,6 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
     const f32x2 v = {lo, hi};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-}
-__device__ __forceinline__ float half_sum(float x) {  // x + x of lane ^ 32
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Global offset (within the tile) of the 16 bytes lane `lane` moves in direct
@@ -127,18 +126,17 @@ __device__ __forceinline__ int tr_lane_offset(int lane, int row_bytes) {
 // ---------------------------------------------------------------------------
 // dQ (and D)
 
+// One workgroup of the dQ work (wg of nwg): stages s0 / s1 hold a K tile and
+// a V tile each.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdParams p) {
+__device__ __forceinline__ void dq_body(const BwdParams& p, char* s0, char* s1, int wg, int nwg) {
     using G = BwdGeo<D>;
-    constexpr int STAGE = 2 * G::T_ALLOC;  // K tile, V tile
-    __shared__ __attribute__((aligned(16))) char s0[STAGE];
-    __shared__ __attribute__((aligned(16))) char s1[STAGE];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, hl = lane >> 5, ql = lane & 31;
 
-    const Tile t = map_workgroup<CAUSAL>(p.f);
+    const Tile t = map_workgroup<CAUSAL>(p.f, wg, nwg);
     const int q0 = t.tile * kBR;
     const int q0w = q0 + wave * 32;
     const int qrow = q0w + ql;
@@ -163,35 +161,25 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdParams p) {
         load_rows<D>(s0 + G::T_ALLOC, vb, 0, kv_len, src, wave);
     }
 
-    // Q, dO and O rows of this lane (chunk c: d = 16c + 8h .. + 7)
+    // Q and dO rows of this lane (chunk c: d = 16c + 8h .. + 7)
     bf16x8 qf[G::DCH], dof[G::DCH];
-    float dsum = 0.f;
     {
         const uint32_t row_off = (uint32_t)qrow * (D * 2) + hl * 16;
         const uint32_t bytes = (uint32_t)N * (D * 2);
         const __amdgpu_buffer_rsrc_t qr = make_rsrc(static_cast<const uint16_t*>(p.f.q) + qo_head * D, bytes);
         const __amdgpu_buffer_rsrc_t dr = make_rsrc(static_cast<const uint16_t*>(p.dout) + qo_head * D, bytes);
-        const __amdgpu_buffer_rsrc_t orr = make_rsrc(static_cast<const uint16_t*>(p.o) + qo_head * D, bytes);
 #pragma unroll
         for (int c = 0; c < G::DCH; ++c) {
             qf[c] = __builtin_bit_cast(bf16x8, buf_load16(qr, row_off + c * 32));
-            const uint4 du = buf_load16(dr, row_off + c * 32);
-            const uint4 ou = buf_load16(orr, row_off + c * 32);
-            dof[c] = __builtin_bit_cast(bf16x8, du);
-            const uint32_t dw[4] = {du.x, du.y, du.z, du.w}, ow[4] = {ou.x, ou.y, ou.z, ou.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                dsum = __builtin_fmaf(__uint_as_float(dw[e] << 16), __uint_as_float(ow[e] << 16), dsum);
-                dsum = __builtin_fmaf(__uint_as_float(dw[e] & 0xffff0000u), __uint_as_float(ow[e] & 0xffff0000u), dsum);
-            }
+            dof[c] = __builtin_bit_cast(bf16x8, buf_load16(dr, row_off + c * 32));
         }
     }
-    const float Drow = half_sum(dsum);
     float L2 = __builtin_inff();  // base-2 LSE; +inf (P = 0) for rows without keys or past N
+    float Drow = 0.f;             // D of this row (attn_bwd_delta_kernel)
     if (qrow < N) {
         const float l = p.f.lse[qo_head + qrow];
         if (l != -__builtin_inff()) L2 = l * kLog2e;
-        if (hl == 0) p.delta[qo_head + qrow] = Drow;
+        Drow = p.delta[qo_head + qrow];
     }
     const float c2 = p.scale * kLog2e;
 
@@ -286,12 +274,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dq_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------
 // dK, dV
 
+// One workgroup of the dK/dV work (wg: its index within that work): stages
+// s0 / s1 hold a Q tile, a dO tile and their 64 LSE and D values each.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkv_kernel(BwdParams p) {
+__device__ __forceinline__ void dkv_body(const BwdParams& p, char* s0, char* s1, int wg) {
     using G = BwdGeo<D>;
-    constexpr int STAGE = 2 * G::T_ALLOC + 2048;  // Q tile, dO tile, LSE, D
-    __shared__ __attribute__((aligned(16))) char s0[STAGE];
-    __shared__ __attribute__((aligned(16))) char s1[STAGE];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -308,13 +295,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkv_kernel(BwdParams p) 
     const int heads = p.f.B * Hkv;
     int bg, kt;
     if (heads % kXcds == 0) {  // then every XCD holds heads/8 heads × ktiles workgroups
-        const int x = blockIdx.x % kXcds, k = blockIdx.x / kXcds;
+        const int x = wg % kXcds, k = wg / kXcds;
         const int nh = heads / kXcds;
         kt = k / nh;
         bg = x * nh + k % nh;
     } else {
-        kt = blockIdx.x / heads;
-        bg = blockIdx.x % heads;
+        kt = wg / heads;
+        bg = wg % heads;
     }
     const int g = bg / p.f.B, b = bg - g * p.f.B;
     const int k0 = kt * kBR;
@@ -476,12 +463,65 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkv_kernel(BwdParams p) 
     }
 }
 
+// ---------------------------------------------------------------------------
+// D, then dQ and dK/dV in one launch
+
+// D_i = Σ_d dO_i,d · O_i,d for every query row (fp32), read by both gradient
+// parts.  D / 8 consecutive lanes share a row, 16 bytes of each tensor per
+// lane (coalesced), and add their partial sums through lane exchanges; the
+// grid strides over the rows (the lanes of a row always loop together).
+template <int D>
+__global__ __launch_bounds__(256) void attn_bwd_delta_kernel(const uint16_t* o, const uint16_t* dout, float* delta,
+                                                             int64_t rows) {
+    constexpr int T = D / 8;  // lanes per row (divides 64, so a row never straddles waves)
+    const int part = threadIdx.x % T;
+    const int64_t stride = (int64_t)gridDim.x * (256 / T);
+    for (int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) / T; row < rows; row += stride) {
+        const uint4 a = *reinterpret_cast<const uint4*>(o + row * D + part * 8);
+        const uint4 b = *reinterpret_cast<const uint4*>(dout + row * D + part * 8);
+        const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc = __builtin_fmaf(__uint_as_float(bw[e] << 16), __uint_as_float(aw[e] << 16), acc);
+            acc = __builtin_fmaf(__uint_as_float(bw[e] & 0xffff0000u), __uint_as_float(aw[e] & 0xffff0000u), acc);
+        }
+#pragma unroll
+        for (int m = T / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+        if (part == 0) delta[row] = acc;
+    }
+}
+
+// The dQ workgroups (ndq of them, padded to npad, a multiple of the XCD
+// count, so that the dK/dV workgroups keep their XCD placement) and the dK/dV
+// workgroups in one grid: each CU then runs both kinds side by side, two
+// instruction streams with different vector / matrix mixes, and a small
+// problem fills twice the SIMD slots that either part alone would.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 2) void attn_bwd_kernel(BwdParams p, int ndq, int npad) {
+    using G = BwdGeo<D>;
+    constexpr int STAGE = 2 * G::T_ALLOC + 2048;  // the larger of the two parts' stages
+    __shared__ __attribute__((aligned(16))) char s0[STAGE];
+    __shared__ __attribute__((aligned(16))) char s1[STAGE];
+    const int wg = blockIdx.x;
+    if (wg < npad) {
+        if (wg < ndq) dq_body<D, CAUSAL>(p, s0, s1, wg, ndq);
+    } else {
+        dkv_body<D, CAUSAL>(p, s0, s1, wg - npad);
+    }
+}
+
 template <int D, bool CAUSAL>
 void launch_bwd_d(const BwdParams& p, hipStream_t stream) {
-    const unsigned dq_grid = (unsigned)(p.f.B * p.f.H * p.f.q_tiles);
-    const unsigned dkv_grid = (unsigned)(p.f.B * p.f.Hkv * ((p.f.N + kBR - 1) / kBR));
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, CAUSAL>), dim3(dq_grid), dim3(kThreads), 0, stream, p);
-    hipLaunchKernelGGL((attn_bwd_dkv_kernel<D, CAUSAL>), dim3(dkv_grid), dim3(kThreads), 0, stream, p);
+    const int64_t rows = (int64_t)p.f.B * p.f.H * p.f.N;
+    const unsigned delta_grid = (unsigned)std::min<int64_t>((rows * (D / 8) + 255) / 256, 65536);
+    hipLaunchKernelGGL((attn_bwd_delta_kernel<D>), dim3(delta_grid), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(p.o), static_cast<const uint16_t*>(p.dout), p.delta, rows);
+    const int dq_grid = p.f.B * p.f.H * p.f.q_tiles;
+    const int dq_pad = (dq_grid + kXcds - 1) / kXcds * kXcds;
+    const int dkv_grid = p.f.B * p.f.Hkv * ((p.f.N + kBR - 1) / kBR);
+    hipLaunchKernelGGL((attn_bwd_kernel<D, CAUSAL>), dim3((unsigned)(dq_pad + dkv_grid)), dim3(kThreads), 0, stream, p,
+                       dq_grid, dq_pad);
 }
 
 }  // namespace

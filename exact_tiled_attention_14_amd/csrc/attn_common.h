@@ -92,10 +92,10 @@ struct Tile {
 
 // GEN: the launch may carry several key splits (the plain kernels never do,
 // and skip the arithmetic for them).
+// (w, G: this workgroup's index among the G that share the work; the plain
+// overload takes the launch's own.)
 template <bool CAUSAL, bool GEN = false>
-__device__ __forceinline__ Tile map_workgroup(const Params& p) {
-    const int G = gridDim.x;
-    const int w = blockIdx.x;
+__device__ __forceinline__ Tile map_workgroup(const Params& p, int w, int G) {
     const int x = w % kXcds, k = w / kXcds;
     const int per = G / kXcds, extra = G % kXcds;
     const int logical = x * per + min(x, extra) + k;
@@ -113,6 +113,11 @@ __device__ __forceinline__ Tile map_workgroup(const Params& p) {
     r.b = hb - r.h * p.B;
     r.tile = t;
     return r;
+}
+
+template <bool CAUSAL, bool GEN = false>
+__device__ __forceinline__ Tile map_workgroup(const Params& p) {
+    return map_workgroup<CAUSAL, GEN>(p, (int)blockIdx.x, (int)gridDim.x);
 }
 
 // Number of keys this workgroup must look at: the valid key length of the
