@@ -492,23 +492,24 @@ __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(const uint16_t* o, 
     }
 }
 
-// The dQ workgroups (ndq of them, padded to npad, a multiple of the XCD
-// count, so that the dK/dV workgroups keep their XCD placement) and the dK/dV
-// workgroups in one grid: each CU then runs both kinds side by side, two
-// instruction streams with different vector / matrix mixes, and a small
-// problem fills twice the SIMD slots that either part alone would.
+// The dQ and the dK/dV workgroups in one grid: each CU then runs both kinds
+// side by side, two instruction streams with different vector / matrix
+// mixes, and a small problem fills twice the SIMD slots that either part
+// alone would.  The first part (`first`: 0 = dQ, 1 = dK/dV) has n1 workgroups,
+// padded to npad, a multiple of the XCD count, so that the second part keeps
+// its XCD placement.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void attn_bwd_kernel(BwdParams p, int ndq, int npad) {
+__global__ __launch_bounds__(kThreads, 2) void attn_bwd_kernel(BwdParams p, int first, int n1, int npad) {
     using G = BwdGeo<D>;
     constexpr int STAGE = 2 * G::T_ALLOC + 2048;  // the larger of the two parts' stages
     __shared__ __attribute__((aligned(16))) char s0[STAGE];
     __shared__ __attribute__((aligned(16))) char s1[STAGE];
     const int wg = blockIdx.x;
-    if (wg < npad) {
-        if (wg < ndq) dq_body<D, CAUSAL>(p, s0, s1, wg, ndq);
-    } else {
-        dkv_body<D, CAUSAL>(p, s0, s1, wg - npad);
-    }
+    const bool in_first = wg < npad;
+    if (in_first && wg >= n1) return;  // padding
+    const int idx = in_first ? wg : wg - npad;
+    if (in_first == (first == 0)) dq_body<D, CAUSAL>(p, s0, s1, idx, in_first ? n1 : (int)gridDim.x - npad);
+    else dkv_body<D, CAUSAL>(p, s0, s1, idx);
 }
 
 template <int D, bool CAUSAL>
@@ -518,10 +519,15 @@ void launch_bwd_d(const BwdParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((attn_bwd_delta_kernel<D>), dim3(delta_grid), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(p.o), static_cast<const uint16_t*>(p.dout), p.delta, rows);
     const int dq_grid = p.f.B * p.f.H * p.f.q_tiles;
-    const int dq_pad = (dq_grid + kXcds - 1) / kXcds * kXcds;
     const int dkv_grid = p.f.B * p.f.Hkv * ((p.f.N + kBR - 1) / kBR);
-    hipLaunchKernelGGL((attn_bwd_kernel<D, CAUSAL>), dim3((unsigned)(dq_pad + dkv_grid)), dim3(kThreads), 0, stream, p,
-                       dq_grid, dq_pad);
+    // Longer workgroups first: a dK/dV workgroup walks every query head of its
+    // group, so with grouped heads (or no causal mask, measured) it goes first;
+    // causal without grouping keeps dQ first.
+    const int first = (p.f.H > p.f.Hkv || !CAUSAL) ? 1 : 0;
+    const int n1 = first ? dkv_grid : dq_grid, n2 = first ? dq_grid : dkv_grid;
+    const int npad = (n1 + kXcds - 1) / kXcds * kXcds;
+    hipLaunchKernelGGL((attn_bwd_kernel<D, CAUSAL>), dim3((unsigned)(npad + n2)), dim3(kThreads), 0, stream, p, first,
+                       n1, npad);
 }
 
 }  // namespace
