@@ -182,6 +182,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
+// max(m, x) as the median of (m, x, +∞): fmaxf would first canonicalise each
+// raw MFMA result (one more instruction per element); this folds into v_max3.
+__device__ __forceinline__ float max_raw(float m, float x) { return __builtin_amdgcn_fmed3f(m, x, __builtin_inff()); }
+
 // max / sum of x over the lane pair (lane, lane ^ 32): v_permlane32_swap hands
 // each lane its partner's value in one of the two results, itself in the other.
 __device__ __forceinline__ float pair_max(float x) {
@@ -244,7 +248,7 @@ template <int D, int W>
 __device__ __forceinline__ void softmax_block_exact(const f32x16& s, uint32_t (&pb)[8], WaveState<D, W>& w, float c2) {
     float mx = kNegInf;
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[r], s[r + 1]));
+    for (int r = 0; r < 16; ++r) mx = max_raw(mx, s[r]);
     const float m_new = fmaxf(w.m_run, pair_max(mx) * c2);
     const float m_use = (m_new == kNegInf) ? 0.f : m_new;
     const float lsum = exponentiate(s, pb, c2, m_use);
@@ -325,7 +329,7 @@ __device__ __forceinline__ void tile(WaveState<D, W>& w, const char* stage, cons
             if (MODE == 3 && blk == 0 && first) {
                 float mx = kNegInf;
 #pragma unroll
-                for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sb[r], sb[r + 1]));
+                for (int r = 0; r < 16; ++r) mx = max_raw(mx, sb[r]);
                 w.m_run = pair_max(mx) * c2;
             }
             const float m_use = (w.m_run == kNegInf) ? 0.f : w.m_run;

@@ -252,11 +252,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_fp8_kernel(Params p) {
             // than 2x (base 2: more than 1) above the reference.  Both blocks
             // are then exponentiated against the same reference, since they
             // meet in one P·V product.
+            // (the median of (m, x, +∞) is max(m, x); unlike fmaxf it needs no
+            // canonicalising of the MFMA results first, which tripled the cost)
             float mx = kNegInf;
 #pragma unroll
             for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-                for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[blk][r], s[blk][r + 1]));
+                for (int r = 0; r < 16; ++r) mx = __builtin_amdgcn_fmed3f(mx, s[blk][r], __builtin_inff());
             const float mb = pair_max8(mx) * c2;
             if (__builtin_amdgcn_ballot_w64(mb > m_run + 1.0f) != 0) {
                 const float m_new = fmaxf(m_run, mb);
