@@ -460,13 +460,15 @@ __device__ __forceinline__ void attend_tile(const Params& p, const Tile& t, cons
         // The fast loop from odd j0, two iterations at a time, so that every
         // access names its stage object: the compiler then tells the loads
         // into one stage from the reads of the other and does not wait on
-        // them.  Returns the first iteration it did not run.
+        // them; a last odd iteration still names its stages statically.
+        // Returns the first iteration it did not run.
         auto run_fast = [&](int j0, int j1) __attribute__((always_inline)) {
             int j = j0;
             for (; j + 1 < j1; j += 2) {
                 step(std::integral_constant<int, 1>{}, j, S1, S0);
                 step(std::integral_constant<int, 1>{}, j + 1, S0, S1);
             }
+            if (j < j1) step(std::integral_constant<int, 1>{}, j++, S1, S0);  // (j is odd here)
             return j;
         };
         // Tiles before n_full are unmasked for every wave of the workgroup;
