@@ -88,13 +88,15 @@ def test_many_heads_and_sequences(dev, d, causal):
     check(o, lse, O, L, what)
 
 
+@pytest.mark.parametrize("shape", [(3, 4, 2, 333), (4, 32, 8, 1100)], ids=["small", "large"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-def test_equal_lengths_match_dense_entry_bitwise(dev, d, causal):
+def test_equal_lengths_match_dense_entry_bitwise(dev, shape, d, causal):
     """B sequences of one length packed end to end give bit for bit the dense
     entry point's results on the [B, H, N, d] layout (same kernels, other
-    strides)."""
-    B, H, Hkv, N = 3, 4, 2, 333
+    strides; the large shape has enough tiles for the one-tile-per-workgroup
+    launch, at d = 128 the eight-wave form)."""
+    B, H, Hkv, N = shape
     q, k, v, _ = make_qkv(B, H, Hkv, N, d, "bf16", seed=5)
     scale = float(np.float32(1 / math.sqrt(d)))
     od, lsed = attn.forward(q.to(dev), k.to(dev), v.to(dev), scale=scale, causal=causal)
