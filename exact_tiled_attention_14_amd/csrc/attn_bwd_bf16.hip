@@ -202,8 +202,12 @@ __device__ __forceinline__ void dq_body(const BwdParams& p, char* s0, char* s1, 
             load_rows<D>(next + G::T_ALLOC, vb, kv0 + G::TILE, kv_len, src, wave);
         }
         if (!(CAUSAL && kv0 > q0w + 31)) {  // a wave whose rows all precede the tile skips it
-            // masks only where the tile passes the key length or (causal) this wave's diagonal
-            const bool masked = (kv0 + G::TILE > kv_len) || (CAUSAL && kv0 + G::TILE - 1 > q0w);
+            // masks only where (causal) the tile crosses this wave's diagonal.
+            // Keys past the key length need none: their K rows are loaded as
+            // zeros, so they add nothing to dQ as long as their dS is finite,
+            // which the clamp of P to [0, 1] (a free modifier of v_exp_f32)
+            // ensures; for admissible keys P <= 1 anyway (up to rounding).
+            const bool masked = CAUSAL && kv0 + G::TILE - 1 > q0w;
             const char* ks = cur;
             const char* vs = cur + G::T_ALLOC;
 #pragma unroll
@@ -220,14 +224,14 @@ __device__ __forceinline__ void dq_body(const BwdParams& p, char* s0, char* s1, 
                 }
                 uint32_t dsb[8];
                 // register r holds key kv0 + 32·blk + 8·hl + 16(r / 8) + r % 8;
-                // admissible iff that constant offset is at most lim
-                const int lim = (CAUSAL ? min(kv_len - 1, qrow) : kv_len - 1) - (kv0 + blk * 32 + 8 * hl);
+                // causal: admissible iff that constant offset is at most lim
+                const int lim = qrow - (kv0 + blk * 32 + 8 * hl);
 #pragma unroll
                 for (int r = 0; r < 16; r += 2) {
                     float e[2];
 #pragma unroll
                     for (int u = 0; u < 2; ++u) {
-                        float pr = exp2_fast(__builtin_fmaf(s[r + u], c2, -L2));
+                        float pr = __builtin_amdgcn_fmed3f(exp2_fast(__builtin_fmaf(s[r + u], c2, -L2)), 0.f, 1.f);
                         if (masked) pr = (16 * ((r + u) >> 3) + ((r + u) & 7) <= lim) ? pr : 0.f;
                         e[u] = pr * (dp[r + u] - Drow);
                     }
@@ -370,9 +374,11 @@ __device__ __forceinline__ void dkv_body(const BwdParams& p, char* s0, char* s1,
         const char* dos = cur + G::T_ALLOC;
         const float* lse_s = reinterpret_cast<const float*>(cur + 2 * G::T_ALLOC);
         const float* d_s = reinterpret_cast<const float*>(cur + 2 * G::T_ALLOC + 1024);
-        // masks are needed only where the tile passes the sequence end, the
-        // key length or (causal) the diagonal
-        const bool masked = (r0 + G::TILE > N) || (k0 + kBR > kv_len) || (CAUSAL && k0 + kBR - 1 > r0);
+        // masks only where (causal) the tile crosses the diagonal.  Rows past
+        // the sequence end need none (their Q and dO rows, LSE and D load as
+        // zeros, so they add nothing to dK or dV), nor do keys past the key
+        // length (their rows are zeroed before the store).
+        const bool masked = CAUSAL && k0 + kBR - 1 > r0;
         // under a causal mask a wave whose keys all follow the tile's rows skips it
         if (!(CAUSAL && k0 + wave * 32 > r0 + G::TILE - 1)) {
 #pragma unroll
@@ -391,11 +397,9 @@ __device__ __forceinline__ void dkv_body(const BwdParams& p, char* s0, char* s1,
                 // every row with a key here has a finite LSE (key 0 is admissible)
                 uint32_t pb[8], dsb[8];
                 // register r holds query base + 16(r / 8) + r % 8 with base =
-                // r0 + 32·qb + 8·hl; admissible iff that constant offset lies in
-                // [lo, hi] (q < N, key < key length, and key <= q if causal)
-                const int qbase = r0 + qb * 32 + 8 * hl;
-                const int hi = key < kv_len ? N - 1 - qbase : -1;
-                const int lo = CAUSAL ? key - qbase : 0;
+                // r0 + 32·qb + 8·hl; causal: admissible iff that constant offset
+                // is at least lo (key <= q)
+                const int lo = key - (r0 + qb * 32 + 8 * hl);
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
                     const float4* lp = reinterpret_cast<const float4*>(lse_s + qb * 32 + 16 * hh + 8 * hl);
@@ -411,8 +415,7 @@ __device__ __forceinline__ void dkv_body(const BwdParams& p, char* s0, char* s1,
                             const int r = 8 * hh + u + w2;
                             float pr = exp2_fast(__builtin_fmaf(s[r], c2, -lv[u + w2] * kLog2e));
                             if (masked) {
-                                const int off = 16 * hh + u + w2;
-                                pr = (off >= lo && off <= hi) ? pr : 0.f;
+                                pr = (16 * hh + u + w2 >= lo) ? pr : 0.f;
                             }
                             pe[w2] = pr;
                             de[w2] = pr * (dp[r] - dv8[u + w2]);
@@ -445,6 +448,12 @@ __device__ __forceinline__ void dkv_body(const BwdParams& p, char* s0, char* s1,
     }
     if (t < total) step(t, s0, s1);
 
+    if (key >= kv_len) {  // a padded key: no gradient (its loop terms were not masked)
+#pragma unroll
+        for (int i = 0; i < G::DBLK; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) { dk[i][r] = 0.f; dv[i][r] = 0.f; }
+    }
     if (key < N) {
         uint16_t* dkp = static_cast<uint16_t*>(p.dk) + (kv_head + key) * D;
         uint16_t* dvp = static_cast<uint16_t*>(p.dv) + (kv_head + key) * D;

@@ -42,10 +42,10 @@ def _inputs(B, H, Hkv, N, d, seed):
     return q, k, v, do
 
 
-def run_case(dev, B, H, Hkv, N, d, causal, key_lens, seed, scale=None, poison=False):
+def run_case(dev, B, H, Hkv, N, d, causal, key_lens, seed, scale=None, poison=False, inputs=None):
     what = f"bwd B{B} H{H} Hkv{Hkv} N{N} d{d} causal={causal} key_lens={key_lens} scale={scale}"
     print(what, flush=True)
-    q, k, v, do = _inputs(B, H, Hkv, N, d, seed)
+    q, k, v, do = _inputs(B, H, Hkv, N, d, seed) if inputs is None else inputs
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     scale = float(np.float32(scale))
     kl = None if key_lens is None else torch.tensor(key_lens, dtype=torch.int32)
@@ -95,6 +95,26 @@ def test_backward_padded_with_poison(dev, causal, d):
     for b, n in enumerate(key_lens):
         assert np.all(dk[b, :, n:] == 0) and np.all(dv[b, :, n:] == 0), "padded keys"
     assert np.all(as_f64(dq.cpu())[1] == 0), "sequence without keys"
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_padded_very_negative_scores(dev, causal):
+    """Every admissible score below -100 (so LSE is too): a padded key's zero
+    score would give exp(0 - LSE) > exp(100), beyond fp32.  Its K row is zero,
+    so it may only contribute 0 to dQ, and to nothing else.  (q and k share an
+    opposite offset of the size of their spread, so that dQ, whose component
+    along the offset cancels, stays well conditioned in bf16.)"""
+    B, H, Hkv, N, d = 2, 2, 1, 200, 64
+    g = torch.Generator().manual_seed(21)
+    q = (0.5 + 0.5 * torch.randn(B, H, N, d, generator=g)).to(torch.bfloat16)
+    k = -(0.5 + 0.5 * torch.randn(B, Hkv, N, d, generator=g).abs()).to(torch.bfloat16)
+    v = torch.randn(B, Hkv, N, d, generator=g).to(torch.bfloat16)
+    do = torch.randn(B, H, N, d, generator=g).to(torch.bfloat16)
+    s = (q.double()[:, :, :, None, :] * k.double()[:, :1, None, :, :]).sum(-1) * 8.0
+    assert s.max().item() < -100.0
+    dq, dk, dv = run_case(dev, B, H, Hkv, N, d, causal, [150, 77], seed=0, scale=8.0, inputs=(q, k, v, do))
+    for b, n in enumerate([150, 77]):
+        assert np.all(as_f64(dk.cpu())[b, :, n:] == 0) and np.all(as_f64(dv.cpu())[b, :, n:] == 0), "padded keys"
 
 
 @pytest.mark.parametrize("scale", [0.0, -0.2])
