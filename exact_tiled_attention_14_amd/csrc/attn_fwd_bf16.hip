@@ -305,7 +305,8 @@ __device__ __forceinline__ void qk_block(f32x16& s, const char* ks, const Offset
 // At most two Sᵀ and two P blocks are live.  MODE 1: unmasked tile,
 // reference m kept; MODE 3: reference kept, mask applied when `masked`, and
 // on the group's first tile (`first`) block 0's row max becomes the reference
-// (Oᵀ and ℓ are still zero there); MODE 2: exact running-max update on every
+// (Oᵀ and ℓ are still zero there); MODE 4: MODE 1 on the group's first
+// tile, with that reference; MODE 2: exact running-max update on every
 // block (its α rescale of Oᵀ follows the previous block's Oᵀ MFMAs and
 // precedes this block's).
 template <int D, int W, bool CAUSAL, int MODE>
@@ -322,11 +323,11 @@ __device__ __forceinline__ void tile(WaveState<D, W>& w, const char* stage, cons
         if (blk + 1 < KBLK) qk_block<D, W>(s[(blk + 1) & 1], stage, o, qf, blk + 1);
         if (blk > 0) pv_block<D, W>(w, vs, o, blk - 1, pb[(blk - 1) & 1]);
         f32x16& sb = s[blk & 1];
-        if (MODE != 1 && masked) apply_mask<CAUSAL, W>(sb, blk, kv0, kv_len, qrow, hl);
+        if ((MODE == 2 || MODE == 3) && masked) apply_mask<CAUSAL, W>(sb, blk, kv0, kv_len, qrow, hl);
         if (MODE == 2) {
             softmax_block_exact<D, W>(sb, pb[blk & 1], w, c2);
         } else {
-            if (MODE == 3 && blk == 0 && first) {
+            if ((MODE == 3 && blk == 0 && first) || (MODE == 4 && blk == 0)) {
                 float mx = kNegInf;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mx = max_raw(mx, sb[r]);
@@ -335,7 +336,7 @@ __device__ __forceinline__ void tile(WaveState<D, W>& w, const char* stage, cons
             const float m_use = (w.m_run == kNegInf) ? 0.f : w.m_run;
             w.l_run += exponentiate(sb, pb[blk & 1], c2, m_use);
         }
-        if (MODE == 1) __builtin_amdgcn_sched_barrier(0);  // keep the block pipeline order
+        if (MODE == 1 || MODE == 4) __builtin_amdgcn_sched_barrier(0);  // keep the block pipeline order
     }
     pv_block<D, W>(w, vs, o, KBLK - 1, pb[(KBLK - 1) & 1]);
 }
@@ -433,16 +434,19 @@ __device__ __forceinline__ void attend_tile(const Params& p, const Tile& t, cons
         // Iteration j computes on stage j & 1 while the group's next tile is
         // loaded into the other stage; the barrier closing the iteration
         // makes that stage visible and frees stage j & 1 for the load after.
-        // MODE 1 (fast): every tile is unmasked for every wave; 3: reference
-        // kept, tiles masked where needed, the reference set on the group's
-        // first tile; 2: exact running-max update (the retry pass).
+        // MODE 1 (fast): every tile is unmasked for every wave; 4: the same for
+        // the group's first tile, whose first block sets the reference; 3:
+        // reference kept, tiles masked where needed, the reference set on the
+        // group's first tile; 2: exact running-max update (the retry pass).
+        // (Four-wave groups only: at eight waves the extra copy of the tile
+        // code spills registers.)
         auto step = [&](auto mode_tag, int j, const char* cur, char* next) __attribute__((always_inline)) {
             constexpr int MODE = decltype(mode_tag)::value;
             const int it = KSPLIT * j + grp;
             const int kv0 = it * BC;
             if (it + KSPLIT < ntiles) load_tile<D, W>(o, next, kb, vb, kv0 + KSPLIT * BC, kv_len, ks, wave);
-            if (MODE == 1) {
-                tile<D, W, CAUSAL, 1>(w, cur, o, qf, c2, false, kv0, kv_len, qrow, hl, false);
+            if (MODE == 1 || MODE == 4) {
+                tile<D, W, CAUSAL, MODE>(w, cur, o, qf, c2, false, kv0, kv_len, qrow, hl, true);
             } else if (it < ntiles && !(CAUSAL && kv0 > q0w + 31 + dq)) {
                 // (under a causal mask a wave whose rows all precede the tile skips it)
                 const bool masked = (kv0 + BC > kv_len) || (CAUSAL && kv0 + BC - 1 > q0w + dq);
@@ -481,7 +485,10 @@ __device__ __forceinline__ void attend_tile(const Params& p, const Tile& t, cons
             // that the first tile's masks are not specialised (and kept in
             // registers) for its constant key offset
             for (int j = 0; j < niters;) {
-                run_any(std::integral_constant<int, 3>{}, j, j + 1);
+                if (W == 4 && j == 0 && n_full / KSPLIT > 0)  // an unmasked first tile: the fast code plus the reference
+                    step(std::integral_constant<int, 4>{}, 0, S0, S1);
+                else
+                    run_any(std::integral_constant<int, 3>{}, j, j + 1);
                 j = (j == 0) ? run_fast(1, n_full / KSPLIT) : j + 1;
             }
         }
