@@ -138,7 +138,7 @@ class Runner:
         self.dq = torch.empty_like(self.q)
         self.dk = torch.empty_like(self.k)
         self.dv = torch.empty_like(self.v)
-        self.delta = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=self.q.device)
+        self.delta = torch.empty((2, w.B, w.H, w.N), dtype=torch.float32, device=self.q.device)
         self.bwd_args = (self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), self.o.data_ptr(),
                          self.dout.data_ptr(), self.lse.data_ptr(), self.dq.data_ptr(), self.dk.data_ptr(),
                          self.dv.data_ptr(), self.delta.data_ptr(), w.B, w.H, w.Hkv, w.N, w.d, w.scale,

@@ -382,7 +382,7 @@ def backward(q, k, v, o, lse, dout, *, scale=None, causal=False, key_lens=None, 
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
-    delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    delta = torch.empty((2, B, H, N), dtype=torch.float32, device=q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     st = attn_bwd_bf16(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),

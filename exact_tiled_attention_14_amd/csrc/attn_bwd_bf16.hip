@@ -356,7 +356,8 @@ __device__ __forceinline__ void dkv_body(const BwdParams& p, char* s0, char* s1,
         load_rows<D>(dst, static_cast<const uint16_t*>(p.f.q) + qo_head * D, r0, N, src, wave);
         load_rows<D>(dst + G::T_ALLOC, static_cast<const uint16_t*>(p.dout) + qo_head * D, r0, N, src, wave);
         if (wave == 0) {
-            load_vec64(dst + 2 * G::T_ALLOC, p.f.lse + qo_head, r0, N, lane);
+            // LSE in base-2 units (second half of the scratch, written by attn_bwd_delta_kernel)
+            load_vec64(dst + 2 * G::T_ALLOC, p.delta + (size_t)p.f.B * H * N + qo_head, r0, N, lane);
             load_vec64(dst + 2 * G::T_ALLOC + 1024, p.delta + qo_head, r0, N, lane);
         }
     };
@@ -372,7 +373,7 @@ __device__ __forceinline__ void dkv_body(const BwdParams& p, char* s0, char* s1,
         const int r0 = (qt0 + t % nqt) * G::TILE;
         const char* qs = cur;
         const char* dos = cur + G::T_ALLOC;
-        const float* lse_s = reinterpret_cast<const float*>(cur + 2 * G::T_ALLOC);
+        const float* lse_s = reinterpret_cast<const float*>(cur + 2 * G::T_ALLOC);  // LSE·log2 e
         const float* d_s = reinterpret_cast<const float*>(cur + 2 * G::T_ALLOC + 1024);
         // masks only where (causal) the tile crosses the diagonal.  Rows past
         // the sequence end need none (their Q and dO rows, LSE and D load as
@@ -413,7 +414,7 @@ __device__ __forceinline__ void dkv_body(const BwdParams& p, char* s0, char* s1,
 #pragma unroll
                         for (int w2 = 0; w2 < 2; ++w2) {
                             const int r = 8 * hh + u + w2;
-                            float pr = exp2_fast(__builtin_fmaf(s[r], c2, -lv[u + w2] * kLog2e));
+                            float pr = exp2_fast(__builtin_fmaf(s[r], c2, -lv[u + w2]));
                             if (masked) {
                                 pr = (16 * hh + u + w2 >= lo) ? pr : 0.f;
                             }
@@ -476,12 +477,13 @@ __device__ __forceinline__ void dkv_body(const BwdParams& p, char* s0, char* s1,
 // D, then dQ and dK/dV in one launch
 
 // D_i = Σ_d dO_i,d · O_i,d for every query row (fp32), read by both gradient
-// parts.  D / 8 consecutive lanes share a row, 16 bytes of each tensor per
+// parts, and LSE_i in base-2 units (saves the dK/dV part a multiply per
+// score).  D / 8 consecutive lanes share a row, 16 bytes of each tensor per
 // lane (coalesced), and add their partial sums through lane exchanges; the
 // grid strides over the rows (the lanes of a row always loop together).
 template <int D>
-__global__ __launch_bounds__(256) void attn_bwd_delta_kernel(const uint16_t* o, const uint16_t* dout, float* delta,
-                                                             int64_t rows) {
+__global__ __launch_bounds__(256) void attn_bwd_delta_kernel(const uint16_t* o, const uint16_t* dout, const float* lse,
+                                                             float* delta, int64_t rows) {
     constexpr int T = D / 8;  // lanes per row (divides 64, so a row never straddles waves)
     const int part = threadIdx.x % T;
     const int64_t stride = (int64_t)gridDim.x * (256 / T);
@@ -497,7 +499,10 @@ __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(const uint16_t* o, 
         }
 #pragma unroll
         for (int m = T / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
-        if (part == 0) delta[row] = acc;
+        if (part == 0) {
+            delta[row] = acc;
+            delta[rows + row] = lse[row] * kLog2e;  // (−∞ stays −∞)
+        }
     }
 }
 
@@ -526,7 +531,7 @@ void launch_bwd_d(const BwdParams& p, hipStream_t stream) {
     const int64_t rows = (int64_t)p.f.B * p.f.H * p.f.N;
     const unsigned delta_grid = (unsigned)std::min<int64_t>((rows * (D / 8) + 255) / 256, 65536);
     hipLaunchKernelGGL((attn_bwd_delta_kernel<D>), dim3(delta_grid), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(p.o), static_cast<const uint16_t*>(p.dout), p.delta, rows);
+                       static_cast<const uint16_t*>(p.o), static_cast<const uint16_t*>(p.dout), p.f.lse, p.delta, rows);
     const int dq_grid = p.f.B * p.f.H * p.f.q_tiles;
     const int dkv_grid = p.f.B * p.f.Hkv * ((p.f.N + kBR - 1) / kBR);
     // Longer workgroups first: a dK/dV workgroup walks every query head of its

@@ -64,7 +64,7 @@ struct BwdParams {
     void* dq;
     void* dk;
     void* dv;
-    float* delta;  // [B][H][N] fp32: D_i = Σ_d dO_i,d O_i,d (written, then read)
+    float* delta;  // [2][B][H][N] fp32: D_i = Σ_d dO_i,d O_i,d, then LSE_i·log2 e (written, then read)
     float scale;   // as passed (any finite value)
 };
 

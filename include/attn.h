@@ -180,7 +180,8 @@ size_t attn_splitkv_workspace_bytes(int B, int H, int Nq, int d, int num_splits)
  * Inputs q, k, v, o, dout (bf16) and lse (fp32) in the layouts above; o and lse
  * must be this library's forward results for the same arguments.  Outputs
  * dq [B][H][N][d], dk, dv [B][Hkv][N][d] (bf16, every element written; padded
- * keys get 0).  delta: caller-owned fp32 [B][H][N] scratch, overwritten with D.
+ * keys get 0).  delta: caller-owned fp32 [2][B][H][N] scratch, overwritten
+ * with D and with lse·log2(e).
  * Products on bf16 matrix cores with fp32 accumulation; P and dS are rounded
  * to bf16 as operands.  Any finite scale.  Two kernels are enqueued on
  * `stream` in order; same validation and status codes as attn_fwd_bf16 (q, k,
