@@ -33,6 +33,7 @@
 // MFMA output registers 8c .. 8c + 7 of a half-wave cover 8 consecutive
 // rows, which is the B-operand order of the second product.
 #include <algorithm>
+#include <type_traits>
 
 #include "attn_common.h"
 
@@ -195,7 +196,8 @@ __device__ __forceinline__ void dq_body(const BwdParams& p, char* s0, char* s1, 
     wait_loads();
     __syncthreads();
 
-    auto step = [&](int j, const char* cur, char* next) __attribute__((always_inline)) {
+    auto step = [&](auto mask_tag, int j, const char* cur, char* next) __attribute__((always_inline)) {
+        constexpr bool MASKS = decltype(mask_tag)::value;  // (false: no tile of this trip needs masks)
         const int kv0 = j * G::TILE;
         if (j + 1 < ntiles) {
             load_rows<D>(next, kb, kv0 + G::TILE, kv_len, src, wave);
@@ -207,7 +209,7 @@ __device__ __forceinline__ void dq_body(const BwdParams& p, char* s0, char* s1, 
             // zeros, so they add nothing to dQ as long as their dS is finite,
             // which the clamp of P to [0, 1] (a free modifier of v_exp_f32)
             // ensures; for admissible keys P <= 1 anyway (up to rounding).
-            const bool masked = CAUSAL && kv0 + G::TILE - 1 > q0w;
+            const bool masked = MASKS && CAUSAL && kv0 + G::TILE - 1 > q0w;
             const char* ks = cur;
             const char* vs = cur + G::T_ALLOC;
 #pragma unroll
@@ -254,12 +256,19 @@ __device__ __forceinline__ void dq_body(const BwdParams& p, char* s0, char* s1, 
     // two tiles per trip so that every LDS access names its stage object
     // (the compiler then does not wait for the loads into one stage before
     // reading the other)
+    // key tiles before n_free lie below the diagonal of every wave: their
+    // code carries no mask at all
+    const int n_free = CAUSAL ? min(ntiles, (q0 + 1) / G::TILE) : ntiles;
     int j = 0;
-    for (; j + 1 < ntiles; j += 2) {
-        step(j, s0, s1);
-        step(j + 1, s1, s0);
+    for (; j + 1 < n_free; j += 2) {
+        step(std::false_type{}, j, s0, s1);
+        step(std::false_type{}, j + 1, s1, s0);
     }
-    if (j < ntiles) step(j, s0, s1);
+    for (; j + 1 < ntiles; j += 2) {
+        step(std::true_type{}, j, s0, s1);
+        step(std::true_type{}, j + 1, s1, s0);
+    }
+    if (j < ntiles) step(std::true_type{}, j, s0, s1);
 
     if (qrow < N) {
         uint16_t* dq = static_cast<uint16_t*>(p.dq) + (qo_head + qrow) * D;
