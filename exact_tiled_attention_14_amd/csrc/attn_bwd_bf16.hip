@@ -358,9 +358,28 @@ __device__ __forceinline__ void dkv_body(const BwdParams& p, char* s0, char* s1,
     for (int i = 0; i < G::TI; ++i) src[i] = tile_src<D>(wave, lane, i);
     const float c2 = p.scale * kLog2e;
 
+    // tile order: under a causal mask (at d = 64; see the loops below) first
+    // the mq query tiles of every head that cross the diagonal (the only ones
+    // with masks), then the rest
+    const int mq = (CAUSAL && D == 64) ? min(nqt, (kBR + G::TILE - 1) / G::TILE) : 0;
+    const int n_mask = GR * mq;
+    const int nfree = max(nqt - mq, 1);
+    auto tile_of = [&](int t, int* h, int* r0) __attribute__((always_inline)) {
+        int hi, qi;
+        if (t < n_mask) {
+            hi = t / mq;
+            qi = t - hi * mq;
+        } else {
+            const int u = t - n_mask;
+            hi = u / nfree;
+            qi = mq + (u - hi * nfree);
+        }
+        *h = g * GR + hi;
+        *r0 = (qt0 + qi) * G::TILE;
+    };
     auto issue = [&](int t, char* dst) __attribute__((always_inline)) {
-        const int h = g * GR + t / nqt;
-        const int r0 = (qt0 + t % nqt) * G::TILE;
+        int h, r0;
+        tile_of(t, &h, &r0);
         const size_t qo_head = (size_t)(b * H + h) * N;
         load_rows<D>(dst, static_cast<const uint16_t*>(p.f.q) + qo_head * D, r0, N, src, wave);
         load_rows<D>(dst + G::T_ALLOC, static_cast<const uint16_t*>(p.dout) + qo_head * D, r0, N, src, wave);
@@ -377,9 +396,11 @@ __device__ __forceinline__ void dkv_body(const BwdParams& p, char* s0, char* s1,
     const int a_rd = swap23(ql) * G::ROW + hl * 16;
     const int tr_off = tr_lane_offset(lane, G::ROW);
 
-    auto step = [&](int t, const char* cur, char* next) __attribute__((always_inline)) {
+    auto step = [&](auto mask_tag, int t, const char* cur, char* next) __attribute__((always_inline)) {
+        constexpr bool MASKS = decltype(mask_tag)::value;  // (false: a tile past the masked ones)
         if (t + 1 < total) issue(t + 1, next);
-        const int r0 = (qt0 + t % nqt) * G::TILE;
+        int h_unused, r0;
+        tile_of(t, &h_unused, &r0);
         const char* qs = cur;
         const char* dos = cur + G::T_ALLOC;
         const float* lse_s = reinterpret_cast<const float*>(cur + 2 * G::T_ALLOC);  // LSE·log2 e
@@ -388,7 +409,7 @@ __device__ __forceinline__ void dkv_body(const BwdParams& p, char* s0, char* s1,
         // the sequence end need none (their Q and dO rows, LSE and D load as
         // zeros, so they add nothing to dK or dV), nor do keys past the key
         // length (their rows are zeroed before the store).
-        const bool masked = CAUSAL && k0 + kBR - 1 > r0;
+        const bool masked = MASKS && CAUSAL && k0 + kBR - 1 > r0;
         // under a causal mask a wave whose keys all follow the tile's rows skips it
         if (!(CAUSAL && k0 + wave * 32 > r0 + G::TILE - 1)) {
 #pragma unroll
@@ -451,12 +472,28 @@ __device__ __forceinline__ void dkv_body(const BwdParams& p, char* s0, char* s1,
         wait_loads();
         __syncthreads();
     };
+    // (tile t always computes in stage t & 1: s0 for even t).  At d = 128 the
+    // extra copies of the tile code would spill registers: one loop there.
     int t = 0;
-    for (; t + 1 < total; t += 2) {
-        step(t, s0, s1);
-        step(t + 1, s1, s0);
+    if constexpr (D == 128) {
+        for (; t + 1 < total; t += 2) {
+            step(std::true_type{}, t, s0, s1);
+            step(std::true_type{}, t + 1, s1, s0);
+        }
+        if (t < total) step(std::true_type{}, t, s0, s1);
+    } else {
+        for (; t + 1 < n_mask; t += 2) {
+            step(std::true_type{}, t, s0, s1);
+            step(std::true_type{}, t + 1, s1, s0);
+        }
+        if (t < n_mask) step(std::true_type{}, t++, s0, s1);
+        if ((t & 1) && t < total) step(std::false_type{}, t++, s1, s0);
+        for (; t + 1 < total; t += 2) {
+            step(std::false_type{}, t, s0, s1);
+            step(std::false_type{}, t + 1, s1, s0);
+        }
+        if (t < total) step(std::false_type{}, t, s0, s1);
     }
-    if (t < total) step(t, s0, s1);
 
     if (key >= kv_len) {  // a padded key: no gradient (its loop terms were not masked)
 #pragma unroll
