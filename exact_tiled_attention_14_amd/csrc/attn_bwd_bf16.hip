@@ -12,8 +12,9 @@
 // (the chain rule through the definition; grouped query heads add their dK
 // and dV into their kv head).  Two kernels, both on v_mfma_f32_32x32x16_bf16
 // with fp32 accumulation, P and dS rounded to bf16 as MFMA operands.
-// attn_bwd_delta_kernel first writes D_i (the `delta` buffer); then one
-// launch of attn_bwd_kernel runs both gradient parts side by side:
+// attn_bwd_delta_kernel first writes D_i and LSE_i·log2 e (the `delta`
+// scratch); then one launch of attn_bwd_kernel runs both gradient parts side
+// by side:
 //
 // * dQ workgroups — query-major, the forward kernel's layout: a wave owns
 //   32 query rows (Q and dO rows in registers as B operands) and streams K/V
@@ -21,14 +22,16 @@
 //   dQᵀ += Kᵀ·dSᵀ with Kᵀ read through ds_read_b64_tr_b16.
 // * dK/dV workgroups — key-major: a wave owns 32 keys (K and V rows in
 //   registers as B operands) and streams, for every query head of the kv
-//   head's group, Q/dO tiles of 64 rows (with their LSE and D) through LDS:
+//   head's group, Q/dO tiles of 64 rows (with their base-2 LSE and D) through LDS:
 //   S = Q·Kᵀ, dP = dO·Vᵀ, dS, then dVᵀ += dOᵀ·P and dKᵀ += Qᵀ·dS with dOᵀ
 //   and Qᵀ read through ds_read_b64_tr_b16.  No atomics: every output row is
 //   owned by one wave.
 //
 // Both stream their tiles straight into LDS (buffer_load_dwordx4 … lds) in
 // rows padded to 2d + 16 bytes; reads past a descriptor's end (key length,
-// sequence end) return zeros, so padding never reaches the sums.  A lane
+// sequence end) return zeros, so padding never reaches the sums (padded keys
+// add 0 to dQ through their zero K rows, their own dK/dV rows are zeroed,
+// and only the causal diagonal needs a mask).  A lane
 // reads operand row swap23(lane % 32) (bits 2 and 3 exchanged) so that the
 // MFMA output registers 8c .. 8c + 7 of a half-wave cover 8 consecutive
 // rows, which is the B-operand order of the second product.
