@@ -361,10 +361,9 @@ __device__ __forceinline__ void dkv_body(const BwdParams& p, char* s0, char* s1,
     for (int i = 0; i < G::TI; ++i) src[i] = tile_src<D>(wave, lane, i);
     const float c2 = p.scale * kLog2e;
 
-    // tile order: under a causal mask (at d = 64; see the loops below) first
-    // the mq query tiles of every head that cross the diagonal (the only ones
-    // with masks), then the rest
-    const int mq = (CAUSAL && D == 64) ? min(nqt, (kBR + G::TILE - 1) / G::TILE) : 0;
+    // tile order: under a causal mask first the mq query tiles of every head
+    // that cross the diagonal (the only ones with masks), then the rest
+    const int mq = CAUSAL ? min(nqt, (kBR + G::TILE - 1) / G::TILE) : 0;
     const int n_mask = GR * mq;
     const int nfree = max(nqt - mq, 1);
     auto tile_of = [&](int t, int* h, int* r0) __attribute__((always_inline)) {
@@ -475,15 +474,18 @@ __device__ __forceinline__ void dkv_body(const BwdParams& p, char* s0, char* s1,
         wait_loads();
         __syncthreads();
     };
-    // (tile t always computes in stage t & 1: s0 for even t).  At d = 128 the
-    // extra copies of the tile code would spill registers: one loop there.
+    // (tile t always computes in stage t & 1: s0 for even t).  At d = 128 a
+    // second unrolled copy of the masked tile code would spill registers.
     int t = 0;
     if constexpr (D == 128) {
+        // the few masked tiles through one copy that names its stages at run time
+        for (; t < n_mask; ++t) step(std::true_type{}, t, (t & 1) ? s1 : s0, (t & 1) ? s0 : s1);
+        if ((t & 1) && t < total) step(std::false_type{}, t++, s1, s0);
         for (; t + 1 < total; t += 2) {
-            step(std::true_type{}, t, s0, s1);
-            step(std::true_type{}, t + 1, s1, s0);
+            step(std::false_type{}, t, s0, s1);
+            step(std::false_type{}, t + 1, s1, s0);
         }
-        if (t < total) step(std::true_type{}, t, s0, s1);
+        if (t < total) step(std::false_type{}, t, s0, s1);
     } else {
         for (; t + 1 < n_mask; t += 2) {
             step(std::true_type{}, t, s0, s1);
