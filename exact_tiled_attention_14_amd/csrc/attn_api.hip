@@ -15,6 +15,8 @@ hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool causal, hipStream_t s
 hipError_t launch_fwd_fp8(const Params& p, int d, bool causal, hipStream_t stream);
 hipError_t launch_merge(const float* o_parts, const float* lse_parts, int S, int64_t rows, int d, void* o,
                         bool o_bf16, float* lse, hipStream_t stream);
+hipError_t launch_merge_bf16_parts(const uint16_t* o_parts, const float* lse_parts, int S, int64_t rows, int d,
+                                   void* o, float* lse, hipStream_t stream);
 }  // namespace attn
 
 namespace {
@@ -243,7 +245,8 @@ int split_chunk(int N, int S) {
 
 size_t attn_splitkv_workspace_bytes(int B, int H, int N, int d, int num_splits) {
     if (B < 0 || H < 1 || N < 0 || (d != 64 && d != 128) || num_splits < 1 || num_splits > ATTN_MAX_SPLITS) return 0;
-    return (size_t)num_splits * B * H * N * (d + 1) * sizeof(float);
+    // bf16 partial O, then fp32 partial LSE
+    return (size_t)num_splits * B * H * N * (d * 2 + 4);
 }
 
 int attn_fwd_splitkv_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -277,16 +280,15 @@ int attn_fwd_splitkv_bf16(const void* q, const void* k, const void* v, void* o, 
     const size_t need = attn_splitkv_workspace_bytes(B, H, Nq, d, num_splits);
     if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
     if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
-    float* o_parts = static_cast<float*>(workspace);
-    float* lse_parts = o_parts + (size_t)S * B * H * Nq * d;
-    p.o = nullptr;
+    uint16_t* o_parts = static_cast<uint16_t*>(workspace);
+    float* lse_parts = reinterpret_cast<float*>(o_parts + (size_t)S * B * H * Nq * d);
+    p.o = o_parts;  // [S][B][H][Nq][d] bf16 partials
     p.splits = S;
     p.chunk = chunk;
-    p.o_f32 = o_parts;
     p.lse = lse_parts;
     hipError_t e = attn::launch_fwd_bf16(p, d, causal != 0, schedule_bf16(p, causal != 0), hs);
     if (e != hipSuccess) return hip_status(e);
-    e = attn::launch_merge(o_parts, lse_parts, S, (int64_t)B * H * Nq, d, o, true, lse, hs);
+    e = attn::launch_merge_bf16_parts(o_parts, lse_parts, S, (int64_t)B * H * Nq, d, o, lse, hs);
     return hip_status(e);
 }
 

@@ -3,9 +3,12 @@
 // Transformer效率", section "闪电注意力的数学原理", formula 2, read as: with
 // LSE = ln Σ_s e^{LSE_s}, O = Σ_s e^{LSE_s − LSE} O_s).
 //
-// Memory-bound: each partial is read once (d fp32 + one fp32 per row) and the
-// result written once; threads take 4 consecutive elements of a row, so
-// consecutive threads read consecutive 16-byte pieces of each partial.
+// Memory-bound: each partial is read once (d fp32 or bf16 values + one fp32
+// LSE per row) and the result written once; threads take 4 consecutive
+// elements of a row, so consecutive threads read consecutive pieces of each
+// partial.  fp32 partials come from attn_fwd_partial_bf16 (the attn_merge
+// entry point); the split-KV forward keeps its partials in bf16 (half the
+// traffic of both the partial writes and this kernel's reads).
 #include "attn_common.h"
 
 namespace attn {
@@ -13,8 +16,8 @@ namespace {
 
 constexpr float kLog2e = 1.44269504088896340736f;
 
-template <bool OUT_BF16>
-__global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ o_parts,
+template <bool OUT_BF16, typename PART>
+__global__ __launch_bounds__(256) void attn_merge_kernel(const PART* __restrict__ o_parts,
                                                          const float* __restrict__ lse_parts, int S, int64_t rows,
                                                          int d, void* __restrict__ o, float* __restrict__ lse) {
     const int per_row = d / 4;
@@ -32,7 +35,14 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
             const float l = lse_parts[(size_t)s * rows + row];
             if (!(l > kNegInf)) continue;  // an empty partial contributes nothing
             const float w = exp2_fast((l - m) * kLog2e);
-            const float4 v = *reinterpret_cast<const float4*>(o_parts + ((size_t)s * rows + row) * d + 4 * c);
+            float4 v;
+            if constexpr (sizeof(PART) == 4) {
+                v = *reinterpret_cast<const float4*>(o_parts + ((size_t)s * rows + row) * d + 4 * c);
+            } else {  // bf16 partials: four values in 8 bytes
+                const uint2 u = *reinterpret_cast<const uint2*>(o_parts + ((size_t)s * rows + row) * d + 4 * c);
+                v = make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                                __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+            }
             wsum += w;
             acc.x += w * v.x;
             acc.y += w * v.y;
@@ -67,9 +77,20 @@ hipError_t launch_merge(const float* o_parts, const float* lse_parts, int S, int
     const int64_t threads = rows * (d / 4);
     const dim3 grid((unsigned)((threads + 255) / 256));
     if (o_bf16)
-        hipLaunchKernelGGL((attn_merge_kernel<true>), grid, dim3(256), 0, stream, o_parts, lse_parts, S, rows, d, o, lse);
+        hipLaunchKernelGGL((attn_merge_kernel<true, float>), grid, dim3(256), 0, stream, o_parts, lse_parts, S, rows, d, o,
+                           lse);
     else
-        hipLaunchKernelGGL((attn_merge_kernel<false>), grid, dim3(256), 0, stream, o_parts, lse_parts, S, rows, d, o, lse);
+        hipLaunchKernelGGL((attn_merge_kernel<false, float>), grid, dim3(256), 0, stream, o_parts, lse_parts, S, rows, d,
+                           o, lse);
+    return hipGetLastError();
+}
+
+hipError_t launch_merge_bf16_parts(const uint16_t* o_parts, const float* lse_parts, int S, int64_t rows, int d,
+                                   void* o, float* lse, hipStream_t stream) {
+    const int64_t threads = rows * (d / 4);
+    const dim3 grid((unsigned)((threads + 255) / 256));
+    hipLaunchKernelGGL((attn_merge_kernel<true, uint16_t>), grid, dim3(256), 0, stream, o_parts, lse_parts, S, rows, d, o,
+                       lse);
     return hipGetLastError();
 }
 

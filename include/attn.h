@@ -150,8 +150,9 @@ int attn_merge(const float* o_parts, const float* lse_parts, int S, int B, int H
 
 /* attn_fwd_splitkv_bf16: attention of Nq queries over Nk keys, the keys cut
  * into num_splits (1 .. ATTN_MAX_SPLITS) ranges of ceil(Nk / num_splits) keys
- * rounded up to a multiple of 128 (so fewer ranges may result), one fp32
- * partial result per range, merged as in attn_merge: two kernels on
+ * rounded up to a multiple of 128 (so fewer ranges may result), one partial
+ * result per range (O in bf16, LSE in fp32, in the workspace), merged as in
+ * attn_merge: two kernels on
  * `stream`.  q, o [B][H][Nq][d] and k, v [B][Hkv][Nk][d] bf16, lse
  * [B][H][Nq] fp32; positions and the causal rule as attn_fwd_partial_bf16
  * (self-attention: Nq = Nk = N, q_offset = k_offset = 0, which is

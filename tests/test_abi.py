@@ -251,7 +251,8 @@ def test_merge_host_validation(over, status):
 
 
 def test_splitkv_workspace_bytes():
-    assert attn.attn_splitkv_workspace_bytes(2, 4, 1000, 64, 3) == 3 * 2 * 4 * 1000 * 65 * 4
+    # bf16 partial O (d values) and an fp32 partial LSE per row and range
+    assert attn.attn_splitkv_workspace_bytes(2, 4, 1000, 64, 3) == 3 * 2 * 4 * 1000 * (64 * 2 + 4)
     assert attn.attn_splitkv_workspace_bytes(2, 4, 1000, 64, 0) == 0
     assert attn.attn_splitkv_workspace_bytes(2, 4, 1000, 64, attn.ATTN_MAX_SPLITS + 1) == 0
     assert attn.attn_splitkv_workspace_bytes(2, 4, 1000, 96, 2) == 0

@@ -3,7 +3,9 @@ oracle: the key-block partial (attn_fwd_partial_bf16), the S-way merge
 (attn_merge) and the split-KV forward (attn_fwd_splitkv_bf16).
 
 Tolerances: O of a bf16-input attention ≤ 1.5e-2 and LSE ≤ 1e-3 (as for the
-dense path; partials are kept in fp32, so the split adds only fp32 rounding);
+dense path; the split-KV forward keeps its partial O in bf16, which adds one
+rounding of 2^-9 relative before the merge, far inside that bound, and its
+partial LSE in fp32);
 the merge of given fp32 partials ≤ 1e-5 (fp32 output) or half a bf16 unit of
 the output magnitude (bf16 output), LSE ≤ 1e-5.
 """
