@@ -77,7 +77,7 @@ TRACE_LABELS = {
     ("attn_fwd_bf16_kernel<128, 4, true, 1, false, true>", 2048):
         "split-KV, 16 ranges: Nq512 over Nk32768 Hq32 Hkv8 d128 causal",
     ("attn_fwd_bf16_kernel<128, 4, true, 2, true, true>", 128): "split-KV shape as one range (persistent)",
-    ("attn_merge_kernel<true>", 2048): "merge of the 16 split-KV partials",
+    ("attn_merge_kernel<true, unsigned short>", 2048): "merge of the 16 split-KV partials (bf16)",
     ("attn_fwd_fp8_kernel<128, true>", 2048): "fp8 forward, workload 4 shape",
     ("attn_fwd_fp8_kernel<128, false>", 4096): "fp8 forward, workload 5 shape",
 }
@@ -143,7 +143,7 @@ Same run as attn_fwd_bf16_workloads2-5_kernel_trace.md:
     {cmd}
 
 Template arguments: attn_fwd_bf16_kernel <D, WAVES, CAUSAL, KSPLIT, PERSISTENT, GENERAL>,
-attn_fwd_fp8_kernel <D, CAUSAL>, attn_merge_kernel <bf16 output>, backward <D, CAUSAL>.
+attn_fwd_fp8_kernel <D, CAUSAL>, attn_merge_kernel <bf16 output, partial type>, backward <D, CAUSAL>.
 Durations in microseconds from run_kernel_trace.csv.
 
 {table(other)}
