@@ -7,17 +7,18 @@ the rocprofv3 commands it names in the summary it writes:
     python3 rocprof_summary.py traffic BASE     # FETCH_SIZE / WRITE_SIZE passes (BASE/tr_*)
     python3 rocprof_summary.py util    BASE     # MFMA-busy passes (BASE/util_W)
 
-The raw runs (one MI355X, repository root, ``export TMPDIR=/tmp``):
+The raw runs (one MI355X, repository root, ``export TMPDIR=/tmp``; OUT is any
+output directory):
 
-    rocprofv3 --kernel-trace --stats -d gpurun_out/kt -o run --output-format csv -- \\
-        python3 bench.py --steps 50 --warmup 5 --no-cpu-baseline > gpurun_out/kt.log
-    rocprofv3 --pmc FETCH_SIZE -d gpurun_out/tr_copy_FETCH_SIZE -o run --output-format csv -- \\
+    rocprofv3 --kernel-trace --stats -d OUT/kt -o run --output-format csv -- \\
+        python3 bench.py --steps 50 --warmup 5 --no-cpu-baseline > OUT/kt.log
+    rocprofv3 --pmc FETCH_SIZE -d OUT/tr_copy_FETCH_SIZE -o run --output-format csv -- \\
         python3 bench.py --copy-calibration 512          (and WRITE_SIZE)
-    rocprofv3 --pmc FETCH_SIZE -d gpurun_out/tr_FETCH_SIZE_W -o run --output-format csv -- \\
+    rocprofv3 --pmc FETCH_SIZE -d OUT/tr_FETCH_SIZE_W -o run --output-format csv -- \\
         python3 bench.py --workload W --steps 3 --warmup 1 --no-extra --no-cpu-baseline \\
         --no-backward --no-varlen --no-splitkv --no-fp8    (W = 2..5, and WRITE_SIZE)
     rocprofv3 --kernel-trace --pmc MfmaUtil SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE \\
-        -d gpurun_out/util_W -o run --output-format csv -- python3 bench.py --workload W \\
+        -d OUT/util_W -o run --output-format csv -- python3 bench.py --workload W \\
         --steps 20 --warmup 2 --no-extra --no-cpu-baseline --no-backward --no-varlen \\
         --no-splitkv --no-fp8                              (W = 2..5)
 
@@ -84,7 +85,7 @@ TRACE_LABELS = {
 
 
 def trace(base, log):
-    cmd = ("rocprofv3 --kernel-trace --stats -d gpurun_out/kt -o run --output-format csv -- "
+    cmd = (f"rocprofv3 --kernel-trace --stats -d {base} -o run --output-format csv -- "
            "python3 bench.py --steps 50 --warmup 5 --no-cpu-baseline")
     groups = collections.OrderedDict()
     for r in csv.DictReader(open(os.path.join(base, "run_kernel_trace.csv"))):
@@ -186,12 +187,12 @@ def traffic(base):
     md = f"""# HBM traffic of attn_fwd_bf16_kernel per launch (rocprofv3 counters)
 
 Commands (one MI355X, repository root; one counter per pass), summarised by
-`python3 rocprof_summary.py traffic gpurun_out`:
+`python3 rocprof_summary.py traffic {base}`:
 
-    rocprofv3 --pmc FETCH_SIZE -d gpurun_out/tr_copy_FETCH_SIZE -o run --output-format csv -- python3 bench.py --copy-calibration 512
-    rocprofv3 --pmc WRITE_SIZE -d gpurun_out/tr_copy_WRITE_SIZE -o run --output-format csv -- python3 bench.py --copy-calibration 512
-    rocprofv3 --pmc FETCH_SIZE -d gpurun_out/tr_FETCH_SIZE_W -o run --output-format csv -- python3 bench.py --workload W --steps 3 --warmup 1 {BENCH_FLAGS}
-    rocprofv3 --pmc WRITE_SIZE -d gpurun_out/tr_WRITE_SIZE_W -o run --output-format csv -- python3 bench.py --workload W --steps 3 --warmup 1 {BENCH_FLAGS}
+    rocprofv3 --pmc FETCH_SIZE -d {base}/tr_copy_FETCH_SIZE -o run --output-format csv -- python3 bench.py --copy-calibration 512
+    rocprofv3 --pmc WRITE_SIZE -d {base}/tr_copy_WRITE_SIZE -o run --output-format csv -- python3 bench.py --copy-calibration 512
+    rocprofv3 --pmc FETCH_SIZE -d {base}/tr_FETCH_SIZE_W -o run --output-format csv -- python3 bench.py --workload W --steps 3 --warmup 1 {BENCH_FLAGS}
+    rocprofv3 --pmc WRITE_SIZE -d {base}/tr_WRITE_SIZE_W -o run --output-format csv -- python3 bench.py --workload W --steps 3 --warmup 1 {BENCH_FLAGS}
 
 Calibration: a device-to-device copy of 512 MiB (`__amd_rocclr_copyBuffer`) reads
 FETCH_SIZE = {f_copy:.0f} KiB and WRITE_SIZE = {w_copy:.0f} KiB, so FETCH_SIZE is scaled by
@@ -233,9 +234,9 @@ def util(base):
     md = f"""# MFMA utilisation and shader clock of attn_fwd_bf16_kernel (rocprofv3 counters)
 
 Command per workload W (one MI355X, repository root), summarised by
-`python3 rocprof_summary.py util gpurun_out`:
+`python3 rocprof_summary.py util {base}`:
 
-    rocprofv3 --kernel-trace --pmc MfmaUtil SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE -d gpurun_out/util_W -o run --output-format csv -- python3 bench.py --workload W --steps 20 --warmup 2 {BENCH_FLAGS}
+    rocprofv3 --kernel-trace --pmc MfmaUtil SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE -d {base}/util_W -o run --output-format csv -- python3 bench.py --workload W --steps 20 --warmup 2 {BENCH_FLAGS}
 
 Per launch: `SQ_VALU_MFMA_BUSY_CYCLES` (summed over the 1024 SIMDs; 32 per 32x32x16 bf16 MFMA)
 / 1024 is the matrix-core busy time of one SIMD; `SQ_BUSY_CYCLES` (summed over the 32 shader
