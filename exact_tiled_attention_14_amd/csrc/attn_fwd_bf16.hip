@@ -206,15 +206,21 @@ struct WaveState {
 
 // P = 2^(S·c − m) of one 32-key block into bf16 pairs; returns this lane's
 // sum of the fp32 P.  Masked scores are −∞ and c > 0, so they give P = 0.
+// The two partial sums start from the first pair sums rather than from 0:
+// every P is ≥ +0, so the result is the same, but the compiler cannot drop
+// an addition of +0 (it is no identity for −0) and would keep two adds.
 __device__ __forceinline__ float exponentiate(const f32x16& s, uint32_t (&pb)[8], float c2, float m_use) {
-    float l0 = 0.f, l1 = 0.f;
+    float l0, l1;
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
         const float e0 = exp2_fast(__builtin_fmaf(s[r], c2, -m_use));
         const float e1 = exp2_fast(__builtin_fmaf(s[r + 1], c2, -m_use));
         pb[r >> 1] = pack_bf16x2(e0, e1);
-        if (r & 2) l1 += e0 + e1;
-        else l0 += e0 + e1;
+        const float t = e0 + e1;
+        if (r == 0) l0 = t;
+        else if (r == 2) l1 = t;
+        else if (r & 2) l1 += t;
+        else l0 += t;
     }
     return l0 + l1;
 }

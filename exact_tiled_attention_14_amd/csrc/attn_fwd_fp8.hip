@@ -270,7 +270,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_fp8_kernel(Params p) {
             }
             const float bias = 7.0f - (m_run == kNegInf ? 0.f : m_run);  // P' = 2^7 · 2^(s·c − m)
             uint32_t pk[8];
-            float l0 = 0.f, l1 = 0.f;
+            float l0, l1;  // seeded with the first pair sums (all P' ≥ +0): no additions of 0 to keep
 #pragma unroll
             for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
@@ -282,8 +282,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_fp8_kernel(Params p) {
                     int w = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
                     w = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, w, true);
                     pk[4 * blk + r / 4] = (uint32_t)w;
-                    l0 += e0 + e1;
-                    l1 += e2 + e3;
+                    if (blk == 0 && r == 0) {
+                        l0 = e0 + e1;
+                        l1 = e2 + e3;
+                    } else {
+                        l0 += e0 + e1;
+                        l1 += e2 + e3;
+                    }
                 }
             l_run += l0 + l1;
             i32x8 pb;
