@@ -453,11 +453,12 @@ __device__ __forceinline__ void attend_tile(const Params& p, const Tile& t, cons
             if (it + KSPLIT < ntiles) load_tile<D, W>(o, next, kb, vb, kv0 + KSPLIT * BC, kv_len, ks, wave);
             if (MODE == 1 || MODE == 4) {
                 tile<D, W, CAUSAL, MODE>(w, cur, o, qf, c2, false, kv0, kv_len, qrow, hl, true);
-                // ℓ is complete here: otherwise the compiler sinks the first
-                // tile's row-sum adds of an unrolled pair into the second
-                // (its exponentials stay live across, and one tile of the pair
-                // carries all the adds)
-                asm volatile("" : "+v"(w.l_run));
+                // eight waves: ℓ is complete here, otherwise the compiler sinks
+                // the first tile's row-sum adds of an unrolled pair into the
+                // second (its exponentials stay live across, and one tile of
+                // the pair carries all the adds); the four-wave persistent
+                // form ran slower with it, so only eight-wave groups have it
+                if constexpr (W == 8) asm volatile("" : "+v"(w.l_run));
             } else if (it < ntiles && !(CAUSAL && kv0 > q0w + 31 + dq)) {
                 // (under a causal mask a wave whose rows all precede the tile skips it)
                 const bool masked = (kv0 + BC > kv_len) || (CAUSAL && kv0 + BC - 1 > q0w + dq);
