@@ -6,14 +6,20 @@ QKᵀ, masks, online softmax, P·V, epilogue) over one batch of a named
 synthetic workload, launched through the C ABI on torch's current stream with
 the inputs already resident in HBM.  Prints ONE JSON line.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
-                    [--no-cpu-baseline] [--no-extra]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 5]
+                    [--repeats 5] [--no-cpu-baseline] [--no-extra] ...
 
-value = 4·B·H·N²·d / time (TFLOP/s, the metric as written) for the headline
-workload (B=4, H=8, N=1024, d=64, bf16, non-causal).  The three long
-bf16 workloads are timed too and reported under "workloads" with both the
-nominal and the algorithmic (causal: N(N+1)/2 pairs, padded: N·Σkey_len
-pairs) rates and their fraction of the bf16 MFMA peak.
+The headline is the grouped-query padded workload (B=2, 32 query heads over 8
+kv heads, N=8192, d=128, bf16, key lengths uniform on N/2..N): the largest
+algorithmic work of the five workloads.  value = 4·B·H·N²·d / time (TFLOP/s,
+the metric as written); the roofline entry uses the algorithmic count (padded:
+N·Σkey_len pairs; causal: N(N+1)/2 pairs per head).  Time per step is the
+median over ``--repeats`` timed regions of exactly ``--steps`` back-to-back
+launches each, bracketed by HIP events on the launch stream.  The other four
+workloads are timed the same way (each region at least ~25 ms) and reported
+under "workloads", with the fraction of the bf16 MFMA peak (fp32 matrix peak
+for the fp32 workload) and the HBM rate of the committed rocprofv3 traffic
+counters against 8 TB/s.
 """
 
 import argparse
@@ -21,6 +27,7 @@ import hashlib
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -31,7 +38,9 @@ METRIC = "attention fwd TFLOP/s (4·B·H·N²·d) and % of bf16 MFMA peak, 1 MI3
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 matrix, published
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA, published
-HEADLINE = 2
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+HEADLINE = 5
+MIN_REGION_MS = 25.0        # each timed region of a non-headline measurement lasts at least this long
 
 
 def nominal_flops(w):
@@ -55,8 +64,12 @@ def algorithmic_bytes(w):
     return (2 * w.B * w.H * w.N * w.d + 2 * w.B * w.Hkv * w.N * w.d) * e + 4 * w.B * w.H * w.N
 
 
-# the sources that decide what the forward bf16 kernel does and how it is launched
-FORWARD_SOURCES = ("attn_api.hip", "attn_common.h", "attn_fwd_bf16.hip")
+def peak_of(w):
+    return PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+
+
+# the sources that decide what the forward kernels do and how they are launched
+FORWARD_SOURCES = ("attn_api.hip", "attn_common.h", "attn_fwd_bf16.hip", "attn_fwd_f32.hip")
 
 
 def kernel_source_hash():
@@ -67,35 +80,42 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def stored_traffic(workload_id):
-    """HBM bytes per launch from the committed rocprofv3 counter runs, or None
-    when they are absent or were taken on another version of the kernels."""
-    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+def _stored(fname, workload_id):
+    """Entry of a committed rocprofv3 summary for this workload, or None when
+    absent or taken on another version of the kernels."""
     try:
-        with open(path) as f:
+        with open(os.path.join(ROOT, "profiles", fname)) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
     if rec.get("kernel_source_hash") != kernel_source_hash():
         return None
-    ent = rec.get("workloads", {}).get(str(workload_id))
+    return rec.get("workloads", {}).get(str(workload_id))
+
+
+def stored_traffic(workload_id):
+    """HBM bytes per launch (FETCH_SIZE and WRITE_SIZE, calibrated on a copy kernel)."""
+    ent = _stored("hbm_traffic.json", workload_id)
     return None if ent is None else ent.get("bytes_per_launch")
 
 
 def stored_mfma_util(workload_id):
-    """Matrix-core busy fraction and effective shader clock of the forward
-    kernel from the committed rocprofv3 counter runs (SQ_VALU_MFMA_BUSY_CYCLES,
-    SQ_BUSY_CYCLES), or None when absent or taken on another kernel version."""
-    path = os.path.join(ROOT, "profiles", "mfma_util.json")
-    try:
-        with open(path) as f:
-            rec = json.load(f)
-    except (OSError, ValueError):
-        return None
-    if rec.get("kernel_source_hash") != kernel_source_hash():
-        return None
-    ent = rec.get("workloads", {}).get(str(workload_id))
+    """Matrix-core busy fraction and effective shader clock (SQ_VALU_MFMA_BUSY_CYCLES,
+    SQ_BUSY_CYCLES)."""
+    ent = _stored("mfma_util.json", workload_id)
     return None if ent is None else {"mfma_busy": ent["mfma_busy"], "clock_ghz": ent["clock_ghz"]}
+
+
+def hbm_entry(traffic, ms, alg_bytes):
+    """HBM rates of one launch against the 8 TB/s peak: from the counted traffic
+    (when stored for this kernel version) and from the compulsory bytes."""
+    s = ms * 1e-3
+    out = {"algorithmic_bytes": alg_bytes, "algorithmic_gbs": round(alg_bytes / s / 1e9, 1),
+           "traffic_bytes": traffic, "traffic_gbs": None, "peak_gbs": PEAK_HBM_GBS, "traffic_frac": None}
+    if traffic is not None:
+        out["traffic_gbs"] = round(traffic / s / 1e9, 1)
+        out["traffic_frac"] = round(traffic / s / 1e9 / PEAK_HBM_GBS, 4)
+    return out
 
 
 class Runner:
@@ -125,6 +145,15 @@ class Runner:
         if st != 0:
             raise RuntimeError(f"attention launch failed with status {st}")
 
+    def outputs(self, heads, rows=None):
+        """GPU O and LSE of the given (b, h) heads (all rows, or the given ones), on the CPU."""
+        outs = []
+        for b, h in heads:
+            o = self.o[b, h] if rows is None else self.o[b, h, rows]
+            l_ = self.lse[b, h] if rows is None else self.lse[b, h, rows]
+            outs.append((o.cpu(), l_.cpu()))
+        return outs
+
     def prepare_backward(self):
         """Forward outputs, a seeded dout and the gradient buffers (bf16 only)."""
         import torch
@@ -150,14 +179,12 @@ class Runner:
         if st != 0:
             raise RuntimeError(f"backward launch failed with status {st}")
 
-    def time(self, steps, warmup, fn=None):
-        """Average milliseconds per launch over `steps` back-to-back launches,
-        bracketed by HIP events recorded on the launch stream."""
+    def region(self, steps, fn):
+        """Milliseconds per launch over one timed region of `steps`
+        back-to-back launches, bracketed by HIP events recorded on the launch
+        stream (the device is idle on both sides)."""
         import torch
 
-        fn = fn or self.launch
-        for _ in range(warmup):
-            fn()
         torch.cuda.synchronize()
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
@@ -167,6 +194,21 @@ class Runner:
         end.record(self.stream)
         torch.cuda.synchronize()
         return start.elapsed_time(end) / steps
+
+    def time(self, steps, warmup, repeats=5, fn=None, min_region_ms=0.0):
+        """Median milliseconds per launch over `repeats` timed regions.
+
+        Each region holds exactly `steps` launches, raised (for the secondary
+        measurements, min_region_ms > 0) until one region lasts at least
+        min_region_ms.  Returns (median ms, steps per region, all region ms)."""
+        fn = fn or self.launch
+        for _ in range(warmup):
+            fn()
+        if min_region_ms > 0:
+            probe = self.region(max(1, min(steps, 5)), fn)
+            steps = max(steps, min(5000, int(math.ceil(min_region_ms / max(probe, 1e-4)))))
+        ms = [self.region(steps, fn) for _ in range(repeats)]
+        return statistics.median(ms), steps, ms
 
 
 class Fp8Runner(Runner):
@@ -224,19 +266,17 @@ class VarlenRunner(Runner):
 
 class SplitKVRunner(Runner):
     """The split-KV shape (attn_fwd_splitkv_bf16) resident on the GPU, with
-    its workspace; ``launch_one`` times the same problem as one key range."""
+    its workspace; splits=1 times the same problem as one key range."""
 
     def __init__(self, spec, dev, splits=None):
         import torch
 
         import exact_tiled_attention_14_amd as attn
+        from workloads import make_splitkv
 
         self.spec = spec
         s = spec
-        g = torch.Generator("cpu").manual_seed(s["seed"])
-        q = torch.randn((s["B"], s["H"], s["Nq"], s["d"]), generator=g).to(torch.bfloat16)
-        k = torch.randn((s["B"], s["Hkv"], s["Nk"], s["d"]), generator=g).to(torch.bfloat16)
-        v = torch.randn((s["B"], s["Hkv"], s["Nk"], s["d"]), generator=g).to(torch.bfloat16)
+        q, k, v = make_splitkv(s)
         self.q, self.k, self.v = q.to(dev), k.to(dev), v.to(dev)
         self.o = torch.empty_like(self.q)
         self.lse = torch.empty((s["B"], s["H"], s["Nq"]), dtype=torch.float32, device=dev)
@@ -258,57 +298,112 @@ class SplitKVRunner(Runner):
         return 4.0 * s["d"] * s["H"] * s["B"] * pairs
 
 
-def cpu_baseline(w, budget_s=10.0):
-    """The fp64 oracle, as it stands, on this host's cores over a bounded sample
-    of the workload: whole (b, h) heads, all query rows, in order, repeating
-    passes over the workload until about ``budget_s`` seconds are spent.
-    Reported in the metric's unit (TFLOP/s of the nominal 4·N²·d count per
-    head)."""
+def host_cores():
+    """Cores this process may run on (the affinity mask, not the machine's count)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(w, wid, gpu_heads, parity_samples, budget_s=15.0):
+    """The fp64 oracle, as it stands, on this host's cores.
+
+    Timing: whole (b, h) heads of the headline workload (all query rows, keys
+    cut at the sequence's key length), in order, until about ``budget_s``
+    seconds are spent, with the BLAS pool set to every core of the affinity
+    mask.  Reported in the metric's unit (TFLOP/s of the nominal 4·N²·d count
+    per head).
+
+    The heads it computes are also compared with the GPU's output for them
+    (``gpu_heads``: {(b, h): (o, lse)} read back after the timed runs), and
+    ``parity_samples`` ({workload id: (workload, inputs, rows, heads, gpu
+    outputs)}) adds a bounded row sample of every other workload: max |ΔO|
+    and |ΔLSE| per workload against the oracle, the quantities the tests
+    bound.  Returns (baseline entry, parity entry)."""
     import numpy as np
+    from threadpoolctl import threadpool_limits
 
     import oracle
     from workloads import as_f64, make_inputs
 
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        cores = os.cpu_count() or 1
+    cores = host_cores()
+    tol_o = {"bf16": 1.5e-2, "f32": 1e-5}
+
+    def errors(o_g, l_g, O, L):
+        fin = np.isfinite(L)
+        el = float(np.max(np.abs(as_f64(l_g)[fin] - L[fin]))) if fin.any() else 0.0
+        return float(np.max(np.abs(as_f64(o_g) - O))), el
+
+    def entry(ww, what, eo, el):
+        return {"rows": what, "max_abs_dO": eo, "max_abs_dLSE": el, "tol_O": tol_o[ww.dtype], "tol_LSE": 1e-3,
+                "ok": bool(eo <= tol_o[ww.dtype] and el <= 1e-3)}
+
     q, k, v, kl = make_inputs(w)
     q, k, v = as_f64(q), as_f64(k), as_f64(v)
     group = w.H // w.Hkv
-    heads = 0
-    t0 = time.perf_counter()
-    done = False
-    while not done:
-        for b in range(w.B):
-            for h in range(w.H):
-                g = h // group
-                oracle.attention(q[b:b + 1, h:h + 1], k[b:b + 1, g:g + 1], v[b:b + 1, g:g + 1],
-                                 w.scale, causal=w.causal,
-                                 key_lens=None if kl is None else [int(kl[b])])
-                heads += 1
-                if time.perf_counter() - t0 >= budget_s:
-                    done = True
-                    break
-            if done:
-                break
-    dt = time.perf_counter() - t0
+    order = [(b, h) for b in range(w.B) for h in range(w.H)]
+    checked = 0
+    err_o = err_l = 0.0
+    with threadpool_limits(limits=cores):
+        t0 = time.perf_counter()
+        heads = 0
+        while time.perf_counter() - t0 < budget_s:
+            b, h = order[heads % len(order)]
+            g = h // group
+            O, L = oracle.attention(q[b:b + 1, h:h + 1], k[b:b + 1, g:g + 1], v[b:b + 1, g:g + 1], w.scale,
+                                    causal=w.causal, key_lens=None if kl is None else [int(kl[b])])
+            if heads < len(order) and (b, h) in gpu_heads:
+                eo, el = errors(*gpu_heads[(b, h)], O[0, 0], L[0, 0])
+                err_o, err_l = max(err_o, eo), max(err_l, el)
+                checked += 1
+            heads += 1
+        dt = time.perf_counter() - t0
+        parity = {str(wid): entry(w, f"{checked} whole heads x {w.N} rows", err_o, err_l)}
+        for sid, (ww, inputs, rows, hs, outs) in sorted(parity_samples.items()):
+            sq, sk, sv, skl = inputs
+            sq, sk, sv = as_f64(sq), as_f64(sk), as_f64(sv)
+            eo = el = 0.0
+            for (b, h), (o_g, l_g) in zip(hs, outs):
+                g = h // (ww.H // ww.Hkv)
+                O, L = oracle.attention(sq[b:b + 1, h:h + 1], sk[b:b + 1, g:g + 1], sv[b:b + 1, g:g + 1], ww.scale,
+                                        causal=ww.causal, key_lens=None if skl is None else [int(skl[b])],
+                                        rows=rows)
+                e1, e2 = errors(o_g, l_g, O[0, 0], L[0, 0])
+                eo, el = max(eo, e1), max(el, e2)
+            parity[str(sid)] = entry(ww, f"{len(hs)} heads x {len(rows)} rows", eo, el)
     flops = 4.0 * heads * w.N * w.N * w.d
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{heads} (b,h) head passes ({heads / (w.B * w.H):.2f} x the {w.B * w.H}-head "
-                      f"workload), all {w.N} query rows each, fp64 numpy, {dt:.1f} s wall",
+    base = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{heads} whole (b,h) heads of the {w.B * w.H}-head workload '{w.name}', all {w.N} query "
+                      f"rows each against the sequence's keys, fp64 numpy with {cores} BLAS threads, "
+                      f"{dt:.1f} s wall",
             "seconds": round(dt, 2)}
+    return base, parity
+
+
+def parity_rows(N, n=96, seed=0):
+    """Rows checked by the bench's parity sample: both ends, tile edges and random rows."""
+    import numpy as np
+
+    fixed = {0, 1, 127, 128, 255, 256, N // 2, N - 129, N - 2, N - 1}
+    rng = np.random.default_rng(seed)
+    rnd = set(rng.choice(N, size=min(n, N), replace=False).tolist())
+    return np.array(sorted(r for r in fixed | rnd if 0 <= r < N))
+
+
+def rate(flops, ms):
+    return flops / (ms * 1e-3) / 1e12
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--repeats", type=int, default=5, help="timed regions per measurement (median reported)")
     ap.add_argument("--workload", type=int, default=HEADLINE)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="skip timing the other bf16 workloads")
+    ap.add_argument("--no-extra", action="store_true", help="skip timing the other workloads")
     ap.add_argument("--no-backward", action="store_true", help="skip timing the backward pass")
     ap.add_argument("--no-varlen", action="store_true", help="skip timing the packed variable-length batch")
     ap.add_argument("--no-splitkv", action="store_true", help="skip timing the split-KV shape")
@@ -319,8 +414,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): the forward pass "
-              "has no multi-GPU path; run with --gpus 1", file=sys.stderr)
+        print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): this build runs on a single "
+              "MI355X and has no multi-GPU path; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -341,18 +436,24 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n, "launches": 3}))
         return
     w = WORKLOADS[args.workload]
+    want_parity = not args.no_cpu_baseline
 
     r = Runner(w, dev)
-    ms = r.time(args.steps, args.warmup)
+    ms, steps, all_ms = r.time(args.steps, args.warmup, args.repeats)
     nom = nominal_flops(w)
     alg = algorithmic_flops(w, r.key_lens_host)
-    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
-    achieved = alg / (ms * 1e-3) / 1e12
+    peak = peak_of(w)
+    achieved = rate(alg, ms)
     traffic = stored_traffic(args.workload)
+    gpu_heads = {}
+    if want_parity:
+        heads = [(b, h) for b in range(w.B) for h in range(w.H)][:24]
+        gpu_heads = dict(zip(heads, r.outputs(heads)))
+    del r
 
     line = {
         "metric": METRIC,
-        "value": round(nom / (ms * 1e-3) / 1e12, 3),
+        "value": round(rate(nom, ms), 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -362,35 +463,49 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
-        "data": "synthetic (seeded i.i.d. N(0,1) q/k/v; no dataset)",
+        "data": "synthetic (seeded i.i.d. N(0,1) q/k/v, key lengths uniform on N/2..N; no dataset)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Hkv": w.Hkv, "N": w.N, "d": w.d,
                    "causal": w.causal, "padded": w.padded, "scale": w.scale},
+        "timing": {"repeats": args.repeats, "steps_per_region": steps, "region_ms_per_step": [round(x, 5)
+                                                                                               for x in all_ms],
+                   "statistic": "median of the regions"},
         "frac_of_bf16_peak": round(achieved / PEAK_BF16_TFLOPS, 4),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "algorithmic_bytes": algorithmic_bytes(w),
                      "algorithmic_flops": alg,
+                     "hbm": hbm_entry(traffic, ms, algorithmic_bytes(w)),
                      "counters": stored_mfma_util(args.workload)},
     }
 
+    parity_samples = {}
     if not args.no_extra:
         extra = {}
-        for wid in (3, 4, 5):
+        for wid in sorted(WORKLOADS):
             if wid == args.workload:
                 continue
             ww = WORKLOADS[wid]
             rr = Runner(ww, dev)
-            steps = max(10, min(args.steps, 100))
-            m = rr.time(steps, max(3, args.warmup // 4))
+            m, st, allm = rr.time(args.steps, max(3, args.warmup // 2), args.repeats, min_region_ms=MIN_REGION_MS)
             a = algorithmic_flops(ww, rr.key_lens_host)
+            pk = peak_of(ww)
+            tr = stored_traffic(wid)
             extra[str(wid)] = {
-                "workload": ww.name, "ms": round(m, 4), "steps": steps,
-                "nominal_tflops": round(nominal_flops(ww) / (m * 1e-3) / 1e12, 2),
-                "algorithmic_tflops": round(a / (m * 1e-3) / 1e12, 2),
-                "frac_of_bf16_peak": round(a / (m * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                "traffic": stored_traffic(wid),
+                "workload": ww.name, "ms": round(m, 5), "steps_per_region": st, "repeats": args.repeats,
+                "region_ms": [round(x, 5) for x in allm],
+                "nominal_tflops": round(rate(nominal_flops(ww), m), 2),
+                "algorithmic_tflops": round(rate(a, m), 2),
+                "peak_tflops": pk,
+                "frac_of_peak": round(rate(a, m) / pk, 4),
+                "peak_kind": "bf16 MFMA" if ww.dtype == "bf16" else "fp32 matrix",
+                "hbm": hbm_entry(tr, m, algorithmic_bytes(ww)),
                 "counters": stored_mfma_util(wid),
             }
+            if want_parity:
+                from workloads import make_inputs
+
+                rows = parity_rows(ww.N, seed=wid)
+                hs = [(0, 0), (ww.B - 1, ww.H - 1)]
+                parity_samples[wid] = (ww, make_inputs(ww), rows, hs, rr.outputs(hs, rows=torch.as_tensor(rows)))
             del rr
         line["workloads"] = extra
 
@@ -398,18 +513,18 @@ def main():
         # backward pass (dq, dk, dv): algorithmic flops = 2.5 x the forward's
         # (five products per admissible (query, key) pair instead of two)
         bwd = {}
-        for wid in (2, 3, 4, 5):
+        for wid in sorted(WORKLOADS):
             ww = WORKLOADS[wid]
             if ww.dtype != "bf16":
                 continue
             rr = Runner(ww, dev)
             rr.prepare_backward()
-            steps = max(5, min(args.steps, 30))
-            m = rr.time(steps, 3, fn=rr.launch_backward)
+            m, st, _ = rr.time(max(5, min(args.steps, 30)), 3, args.repeats, fn=rr.launch_backward,
+                               min_region_ms=MIN_REGION_MS)
             a = 2.5 * algorithmic_flops(ww, rr.key_lens_host)
-            bwd[str(wid)] = {"workload": ww.name, "ms": round(m, 4), "steps": steps,
-                             "algorithmic_tflops": round(a / (m * 1e-3) / 1e12, 2),
-                             "frac_of_bf16_peak": round(a / (m * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+            bwd[str(wid)] = {"workload": ww.name, "ms": round(m, 4), "steps_per_region": st,
+                             "algorithmic_tflops": round(rate(a, m), 2),
+                             "frac_of_bf16_peak": round(rate(a, m) / PEAK_BF16_TFLOPS, 4)}
             del rr
         line["backward"] = bwd
 
@@ -417,12 +532,11 @@ def main():
         from workloads import VARLEN
 
         vr = VarlenRunner(VARLEN, dev)
-        steps = max(5, min(args.steps, 30))
-        m = vr.time(steps, 3)
+        m, st, _ = vr.time(max(5, min(args.steps, 30)), 3, args.repeats, min_region_ms=MIN_REGION_MS)
         a = vr.algorithmic_flops()
-        line["varlen"] = {"workload": VARLEN["name"], "lengths": vr.lengths, "ms": round(m, 4), "steps": steps,
-                          "algorithmic_tflops": round(a / (m * 1e-3) / 1e12, 2),
-                          "frac_of_bf16_peak": round(a / (m * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        line["varlen"] = {"workload": VARLEN["name"], "lengths": vr.lengths, "ms": round(m, 4),
+                          "steps_per_region": st, "algorithmic_tflops": round(rate(a, m), 2),
+                          "frac_of_bf16_peak": round(rate(a, m) / PEAK_BF16_TFLOPS, 4)}
         del vr
 
     if not args.no_fp8:
@@ -431,12 +545,11 @@ def main():
         for wid in (4, 5):
             ww = WORKLOADS[wid]
             fr = Fp8Runner(ww, dev)
-            steps = max(10, min(args.steps, 50))
-            m = fr.time(steps, 3)
+            m, st, _ = fr.time(max(10, min(args.steps, 50)), 3, args.repeats, min_region_ms=MIN_REGION_MS)
             a = algorithmic_flops(ww, fr.key_lens_host)
-            fp8[str(wid)] = {"workload": ww.name.replace("bf16", "fp8 e4m3"), "ms": round(m, 4), "steps": steps,
-                             "algorithmic_tflops": round(a / (m * 1e-3) / 1e12, 2),
-                             "frac_of_fp8_peak": round(a / (m * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4)}
+            fp8[str(wid)] = {"workload": ww.name.replace("bf16", "fp8 e4m3"), "ms": round(m, 4),
+                             "steps_per_region": st, "algorithmic_tflops": round(rate(a, m), 2),
+                             "frac_of_fp8_peak": round(rate(a, m) / PEAK_FP8_TFLOPS, 4)}
             del fr
         line["fp8"] = fp8
 
@@ -446,17 +559,18 @@ def main():
         res = {"workload": SPLITKV["name"]}
         for splits in (1, SPLITKV["splits"]):
             sr = SplitKVRunner(SPLITKV, dev, splits=splits)
-            steps = max(10, min(args.steps, 50))
-            m = sr.time(steps, 3)
+            m, st, _ = sr.time(max(10, min(args.steps, 50)), 3, args.repeats, min_region_ms=MIN_REGION_MS)
             a = sr.algorithmic_flops()
             res["one_range" if splits == 1 else f"{splits}_ranges"] = {
-                "ms": round(m, 4), "steps": steps, "algorithmic_tflops": round(a / (m * 1e-3) / 1e12, 2),
-                "frac_of_bf16_peak": round(a / (m * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+                "ms": round(m, 4), "steps_per_region": st, "algorithmic_tflops": round(rate(a, m), 2),
+                "frac_of_bf16_peak": round(rate(a, m) / PEAK_BF16_TFLOPS, 4)}
             del sr
         line["splitkv"] = res
 
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w)
+    if want_parity:
+        base, parity = cpu_baseline(w, args.workload, gpu_heads, parity_samples)
+        line["cpu_baseline"] = base
+        line["parity"] = parity
 
     print(json.dumps(line), flush=True)
 

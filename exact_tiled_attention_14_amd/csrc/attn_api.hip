@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <stdio.h>
 
+#include <atomic>
+
 #include "attn.h"
 #include "attn_common.h"
 
@@ -78,17 +80,19 @@ int hip_status(hipError_t e) {
     return ATTN_ERR_HIP;
 }
 
-// Number of compute units of the current device (cached per device).
+// Number of compute units of the current device, cached per device.  The
+// cache entries are atomics: concurrent first calls on one device may both
+// query the attribute, and both store the same value.
 int device_cus() {
-    static int cached[64] = {0};
+    static std::atomic<int> cached[64];  // zero-initialised (static storage)
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cached[dev] = n;
+        cached[dev].store(n, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return n;
 }
 
 // Launch shape of the bf16 kernel.  Under a causal mask query tiles differ

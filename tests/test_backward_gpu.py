@@ -18,6 +18,7 @@ import torch
 
 import exact_tiled_attention_14_amd as attn
 import oracle
+from tests.fullsize import parallel_heads
 from workloads import as_f64
 
 pytestmark = pytest.mark.gpu
@@ -161,27 +162,51 @@ def test_backward_workload2_full(dev):
         _compare(f"workload 2 {name}", got, want)
 
 
-def test_backward_workload3_heads(dev):
-    """Workload 3 (causal B2 H8 N4096 d64) at full size; two whole heads
-    against the oracle (each head is its own kv head there)."""
+def test_backward_workload3_all_heads(dev):
+    """Workload 3 (causal B2 H8 N4096 d64) at full size: dQ, dK and dV of all
+    16 heads, every element, against the oracle (each head is its own kv head
+    there; the heads run side by side on the host's cores)."""
     w, (q, k, v, do, kl), (dq, dk, dv) = _workload_backward(dev, 3)
-    for b, h in ((0, 0), (1, 7)):
-        ref = oracle.attention_backward(as_f64(q[b:b + 1, h:h + 1]), as_f64(k[b:b + 1, h:h + 1]),
-                                        as_f64(v[b:b + 1, h:h + 1]), as_f64(do[b:b + 1, h:h + 1]), w.scale,
-                                        causal=True)
-        for name, got, want in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
-            _compare(f"workload 3 b={b} h={h} {name}", got[b:b + 1, h:h + 1], want)
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+
+    def one(bh):
+        b, h = bh
+        return oracle.attention_backward(as_f64(q[b:b + 1, h:h + 1]), as_f64(k[b:b + 1, h:h + 1]),
+                                         as_f64(v[b:b + 1, h:h + 1]), as_f64(do[b:b + 1, h:h + 1]), w.scale,
+                                         causal=True)
+
+    refs = parallel_heads(one, heads)
+    for name, i, got in (("dQ", 0, dq), ("dK", 1, dk), ("dV", 2, dv)):
+        want = np.zeros(got.shape)
+        for (b, h), r in zip(heads, refs):
+            want[b, h] = r[i][0, 0]
+        _compare(f"workload 3 all 16 heads {name}", got, want)
 
 
-@pytest.mark.parametrize("wid", [4, 5])
-def test_backward_long_workloads_column_sums(dev, wid):
-    """Workloads 4 and 5 at full size (too large for the oracle's N x N
-    matrices): a property of the definition that holds at any size.  Each
+def _groups_against_oracle(wid, w, inputs, grads, groups):
+    """Whole kv groups (b, g) of a workload: dQ of the group's query heads and
+    dK, dV of the kv head, every element, against the oracle."""
+    q, k, v, do, kl = inputs
+    dq, dk, dv = grads
+    group = w.H // w.Hkv
+    for b, g in groups:
+        hs = slice(g * group, (g + 1) * group)
+        ref = oracle.attention_backward(as_f64(q[b:b + 1, hs]), as_f64(k[b:b + 1, g:g + 1]),
+                                        as_f64(v[b:b + 1, g:g + 1]), as_f64(do[b:b + 1, hs]), w.scale,
+                                        causal=w.causal, key_lens=None if kl is None else [int(kl[b])])
+        for name, got, want in zip(("dQ", "dK", "dV"), (dq[b:b + 1, hs], dk[b:b + 1, g:g + 1],
+                                                        dv[b:b + 1, g:g + 1]), ref):
+            _compare(f"workload {wid} b={b} kv head {g} ({group} query heads) {name}", got, want)
+
+
+def _column_sums(wid, w, inputs, grads):
+    """A property of the definition at any size, over every kv group: each
     admissible row's weights sum to one, so for every kv head the dV rows
     summed over the keys equal the dO rows summed over that head's query
     heads; padded keys get exactly zero gradients.  Tolerance: the weights
     are bf16 operands (2^-9 each) and dV is stored in bf16."""
-    w, (q, k, v, do, kl), (dq, dk, dv) = _workload_backward(dev, wid)
+    q, k, v, do, kl = inputs
+    dq, dk, dv = grads
     group = w.H // w.Hkv
     do64, dv64 = as_f64(do), as_f64(dv)
     assert not np.isnan(as_f64(dq)).any() and not np.isnan(as_f64(dk)).any() and not np.isnan(dv64).any()
@@ -196,4 +221,24 @@ def test_backward_long_workloads_column_sums(dev, wid):
                 + 2.0 ** -8 * np.abs(dv64[b, g, :n]).sum(axis=0)
             worst = float(np.max(np.abs(got - want) / tol))
             assert worst <= 1.0, f"workload {wid} b={b} g={g}: column sums of dV off by {worst:.2f}x the bound"
-        print(f"  workload {wid} b={b}: dV column sums within bounds", flush=True)
+    print(f"  workload {wid}: dV column sums of every kv group within bounds", flush=True)
+
+
+def test_backward_workload4_heads(dev):
+    """Workload 4 (causal B1 H16 N16384 d128) at full size, in the launch
+    configuration bench.py times: the first and the last head compared
+    element by element with the oracle (each N x N oracle head holds about
+    9 GiB of fp64 matrices), and the column-sum property over every head."""
+    w, inputs, grads = _workload_backward(dev, 4)
+    _groups_against_oracle(4, w, inputs, grads, [(0, 0), (0, w.Hkv - 1)])
+    _column_sums(4, w, inputs, grads)
+
+
+def test_backward_workload5_groups(dev):
+    """Workload 5 (GQA padded B2 Hq32 Hkv8 N8192 d128) at full size: two whole
+    kv groups (4 query heads each; the two sequences have different key
+    lengths) element by element against the oracle, and the column-sum
+    property over every group."""
+    w, inputs, grads = _workload_backward(dev, 5)
+    _groups_against_oracle(5, w, inputs, grads, [(0, 0), (w.B - 1, w.Hkv - 1)])
+    _column_sums(5, w, inputs, grads)

@@ -14,6 +14,7 @@ import torch
 
 import exact_tiled_attention_14_amd as attn
 import oracle
+from tests.fullsize import oracle_all_heads
 from workloads import WORKLOADS, as_f64, make_inputs, make_qkv
 
 pytestmark = pytest.mark.gpu
@@ -95,17 +96,14 @@ def _sample_rows(N, n=192, seed=0):
 @pytest.mark.parametrize("wid", sorted(WORKLOADS))
 def test_workload_full_size(dev, wid):
     """Each named workload at its full size, in the launch configuration the
-    benchmark times; the oracle checks every row of the two small workloads
-    and a row sample (ends, tile edges, random) of the three large ones."""
+    benchmark times: every row of every head against the oracle (the heads run
+    side by side on the host's cores)."""
     w = WORKLOADS[wid]
     print(f"workload {wid}: {w.name}", flush=True)
     q, k, v, kl = make_inputs(w)
     o, lse = run_gpu(dev, q, k, v, w.scale, w.causal, kl)
-    rows = None if w.N <= 1024 else _sample_rows(w.N, seed=wid)
-    O, L = oracle_of(q, k, v, w.scale, w.causal, kl, rows=rows)
-    if rows is not None:
-        o, lse = o[:, :, rows], lse[:, :, rows]
-    check(o, lse, O, L, TOL_O[w.dtype], w.name)
+    O, L = oracle_all_heads(q, k, v, w.scale, w.causal, None if kl is None else kl.tolist())
+    check(o, lse, O, L, TOL_O[w.dtype], f"{w.name}, all {w.B * w.H} heads x {w.N} rows")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])

@@ -18,7 +18,8 @@ import torch
 
 import exact_tiled_attention_14_amd as attn
 import oracle
-from workloads import SPLITKV, as_f64, make_qkv
+from tests.fullsize import parallel_heads
+from workloads import SPLITKV, as_f64, make_qkv, make_splitkv
 
 pytestmark = pytest.mark.gpu
 
@@ -143,22 +144,28 @@ def test_partials_then_merge_equal_dense(dev):
     check(o.cpu(), lse.cpu(), O, L, "two partials merged")
 
 
-def test_splitkv_workload_sampled_rows(dev):
-    """The benchmarked split-KV shape at full size, sampled query rows of
-    every head against the oracle (row sampling is exact)."""
+def test_splitkv_workload_all_heads(dev):
+    """The benchmarked split-KV shape at full size (512 queries at the end of a
+    32768-key sequence, 16 key ranges): every row of every head against the
+    oracle (the heads run side by side on the host's cores)."""
     w = SPLITKV
-    q, k, v = qkv(w["B"], w["H"], w["Hkv"], w["Nq"], w["Nk"], w["d"], seed=w["seed"])
+    q, k, v = make_splitkv(w)
     scale = float(np.float32(1 / math.sqrt(w["d"])))
     o, lse = attn.forward_splitkv(q.to(dev), k.to(dev), v.to(dev), w["splits"], q_offset=w["Nk"] - w["Nq"],
                                   scale=scale, causal=w["causal"])
     torch.cuda.synchronize()
-    rows = np.array([0, 1, 63, 64, 127, 128, 200, w["Nq"] - 1])
-    # one oracle call per sampled row, at that row's position
-    O2, L2 = [], []
-    for r in rows:
-        Or, Lr = oracle.attention_partial(as_f64(q[:, :, r:r + 1]), as_f64(k), as_f64(v), scale, causal=w["causal"],
-                                          q_offset=w["Nk"] - w["Nq"] + int(r))
-        O2.append(Or)
-        L2.append(Lr)
-    O2, L2 = np.concatenate(O2, axis=2), np.concatenate(L2, axis=2)
-    check(o.cpu()[:, :, rows], lse.cpu()[:, :, rows], O2, L2, "split-KV workload rows")
+    q64, k64, v64 = as_f64(q), as_f64(k), as_f64(v)
+    group = w["H"] // w["Hkv"]
+    heads = [(b, h) for b in range(w["B"]) for h in range(w["H"])]
+
+    def one(bh):
+        b, h = bh
+        g = h // group
+        return oracle.attention_partial(q64[b:b + 1, h:h + 1], k64[b:b + 1, g:g + 1], v64[b:b + 1, g:g + 1], scale,
+                                        causal=w["causal"], q_offset=w["Nk"] - w["Nq"])
+
+    O = np.zeros(q.shape)
+    L = np.zeros(q.shape[:3])
+    for (b, h), (ob, lb) in zip(heads, parallel_heads(one, heads)):
+        O[b, h], L[b, h] = ob[0, 0], lb[0, 0]
+    check(o.cpu(), lse.cpu(), O, L, f"split-KV workload, all {len(heads)} heads x {w['Nq']} rows")

@@ -13,6 +13,7 @@ import torch
 
 import exact_tiled_attention_14_amd as attn
 import oracle
+from tests.fullsize import parallel_heads
 from workloads import VARLEN, as_f64, make_qkv, make_varlen, varlen_lengths
 
 pytestmark = pytest.mark.gpu
@@ -155,22 +156,31 @@ def test_empty_pack_is_a_noop(dev):
     assert o.shape == (0, 2, 64) and lse.shape == (2, 0)
 
 
-def test_varlen_workload_sampled_rows(dev):
-    """The benchmarked packed batch at full size: every token computed by the
-    GPU, sampled query rows of every sequence and head checked against the
-    oracle (row sampling is exact: softmax is taken row by row)."""
+def test_varlen_workload_all_heads(dev):
+    """The benchmarked packed batch at full size: every token of every
+    sequence and head against the packed-sequence oracle (each (sequence,
+    head) pair as a one-sequence pack; the pairs run side by side on the
+    host's cores)."""
     w = VARLEN
     lengths = varlen_lengths(w["B"], w["N"] // 2, w["N"], w["seed"])
     q, k, v, cu = make_varlen(lengths, w["H"], w["Hkv"], w["d"], seed=w["seed"])
     scale = float(np.float32(1 / math.sqrt(w["d"])))
     o, lse = run(dev, q, k, v, cu, w["N"], scale, w["causal"])
-    rng = np.random.default_rng(0)
-    for b, n in enumerate(lengths):
-        s0 = int(cu[b])
-        rows = np.unique(np.concatenate([[0, 1, 127, 128, n - 1], rng.integers(0, n, 6)]))
-        qs = q[s0:s0 + n].transpose(0, 1)[None]
-        ks = k[s0:s0 + n].transpose(0, 1)[None]
-        vs = v[s0:s0 + n].transpose(0, 1)[None]
-        O, L = oracle.attention(as_f64(qs), as_f64(ks), as_f64(vs), scale, causal=w["causal"], rows=rows)
-        idx = torch.from_numpy(s0 + rows)
-        check(o[idx].transpose(0, 1)[None], lse[:, idx][None], O, L, f"sequence {b} (length {n})")
+    q64, k64, v64 = as_f64(q), as_f64(k), as_f64(v)
+    group = w["H"] // w["Hkv"]
+    items = [(b, h) for b in range(len(lengths)) for h in range(w["H"])]
+
+    def one(bh):
+        b, h = bh
+        s0, s1 = int(cu[b]), int(cu[b + 1])
+        g = h // group
+        return oracle.attention_varlen(q64[s0:s1, h:h + 1], k64[s0:s1, g:g + 1], v64[s0:s1, g:g + 1], [0, s1 - s0],
+                                       scale, causal=w["causal"])
+
+    O = np.zeros(q.shape)
+    L = np.zeros((w["H"], q.shape[0]))
+    for (b, h), (ob, lb) in zip(items, parallel_heads(one, items)):
+        s0, s1 = int(cu[b]), int(cu[b + 1])
+        O[s0:s1, h] = ob[:, 0]
+        L[h, s0:s1] = lb[0]
+    check(o, lse, O, L, f"packed batch, all {len(lengths)} sequences x {w['H']} heads, every token")

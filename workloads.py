@@ -89,6 +89,17 @@ SPLITKV = dict(name="split-KV chunk Nq512 over Nk32768 Hq32 Hkv8 d128 causal, 16
                B=1, H=32, Hkv=8, Nq=512, Nk=32768, d=128, causal=True, splits=16, seed=7)
 
 
+def make_splitkv(spec):
+    """Inputs of the split-KV shape: a torch.Generator('cpu') seeded with the
+    spec's seed draws q [B, H, Nq, d], then k and v [B, Hkv, Nk, d], as
+    N(0, 1) float32 rounded to bf16 (the recipe above)."""
+    g = torch.Generator("cpu").manual_seed(int(spec["seed"]))
+    q = torch.randn((spec["B"], spec["H"], spec["Nq"], spec["d"]), generator=g).to(torch.bfloat16)
+    k = torch.randn((spec["B"], spec["Hkv"], spec["Nk"], spec["d"]), generator=g).to(torch.bfloat16)
+    v = torch.randn((spec["B"], spec["Hkv"], spec["Nk"], spec["d"]), generator=g).to(torch.bfloat16)
+    return q, k, v
+
+
 def varlen_lengths(B, lo, hi, seed):
     """B sequence lengths drawn uniformly from the integers lo .. hi inclusive
     (a torch.Generator('cpu') seeded with ``seed``)."""
