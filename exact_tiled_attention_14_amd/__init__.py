@@ -3,10 +3,13 @@
 Thin ctypes layer over ``libattn.so`` (see ``include/attn.h``): the functions
 ``attn_fwd_bf16``, ``attn_fwd_f32``, ``attn_fwd``, ``attn_fwd_varlen_bf16``,
 ``attn_fwd_partial_bf16``, ``attn_merge``, ``attn_fwd_splitkv_bf16``,
-``attn_splitkv_workspace_bytes``, ``attn_bwd_bf16`` and ``attn_status_str``
+``attn_splitkv_workspace_bytes``, ``attn_bwd_bf16``, ``attn_fwd_fp8``,
+``attn_fp8_amax``, ``attn_fp8_quantize``, ``attn_fp8_quantize_vt`` and
+``attn_status_str``
 take the same arguments as the C entry points (device pointers as Python
 ints) and return what they return.  ``forward``, ``forward_varlen``,
-``forward_partial``, ``merge``, ``forward_splitkv`` and ``backward`` marshal
+``forward_partial``, ``merge``, ``forward_splitkv``, ``forward_fp8``,
+``quantize_fp8``, ``quantize_fp8_vt`` and ``backward`` marshal
 torch tensors onto them; every step of the computation
 runs in the HIP kernels.  There is no fallback: if the library is missing,
 every call raises.
@@ -18,7 +21,8 @@ import os
 
 __all__ = [
     "AttnError", "attn_fwd", "attn_fwd_bf16", "attn_fwd_f32", "attn_fwd_varlen_bf16", "attn_bwd_bf16",
-    "attn_fwd_fp8", "forward_fp8", "attn_fwd_partial_bf16", "attn_merge", "attn_fwd_splitkv_bf16", "attn_splitkv_workspace_bytes",
+    "attn_fwd_fp8", "forward_fp8", "attn_fp8_amax", "attn_fp8_quantize", "attn_fp8_quantize_vt",
+    "quantize_fp8", "quantize_fp8_vt", "hadamard_signs", "attn_fwd_partial_bf16", "attn_merge", "attn_fwd_splitkv_bf16", "attn_splitkv_workspace_bytes",
     "attn_status_str", "forward", "forward_varlen", "forward_partial", "merge", "forward_splitkv", "backward",
     "library_path", "load_library", "ATTN_ERR_WORKSPACE", "ATTN_MAX_SPLITS",
     "ATTN_OK", "ATTN_ERR_NULL", "ATTN_ERR_SHAPE", "ATTN_ERR_HEAD_DIM", "ATTN_ERR_ALIGN",
@@ -48,6 +52,9 @@ ENTRY_POINTS = {
     "attn_splitkv_workspace_bytes": ([_I] * 5, ctypes.c_size_t),
     "attn_fwd_fp8": ([_P] * 5 + [ctypes.c_float] * 3 + [_I] * 5 + [ctypes.c_float, _I, _P, _P], ctypes.c_int),
     "attn_bwd_bf16": ([_P] * 10 + [_I, _I, _I, _I, _I, ctypes.c_float, _I, _P, _P], ctypes.c_int),
+    "attn_fp8_amax": ([_P, _P, ctypes.c_int64, _I, _P, _P], ctypes.c_int),
+    "attn_fp8_quantize": ([_P, _P, ctypes.c_int64, _I, _P, _P, _P, _P], ctypes.c_int),
+    "attn_fp8_quantize_vt": ([_P, ctypes.c_int64, _I, _I, _P, _P, _P, _P], ctypes.c_int),
     "attn_status_str": ([_I], ctypes.c_char_p),
     "attn_last_hip_error": ([], ctypes.c_char_p),
 }
@@ -120,6 +127,18 @@ def attn_fwd_fp8(q, k, vt, o, lse, q_descale, k_descale, v_descale, B, H, Hkv, N
                  stream):
     return load_library().attn_fwd_fp8(q, k, vt, o, lse, q_descale, k_descale, v_descale, B, H, Hkv, N, d, scale,
                                        causal, key_lens, stream)
+
+
+def attn_fp8_amax(x, signs, rows, d, amax, stream):
+    return load_library().attn_fp8_amax(x, signs, rows, d, amax, stream)
+
+
+def attn_fp8_quantize(x, signs, rows, d, amax, x8, descale, stream):
+    return load_library().attn_fp8_quantize(x, signs, rows, d, amax, x8, descale, stream)
+
+
+def attn_fp8_quantize_vt(v, heads, N, d, amax, vt8, descale, stream):
+    return load_library().attn_fp8_quantize_vt(v, heads, N, d, amax, vt8, descale, stream)
 
 
 def attn_merge(o_parts, lse_parts, S, B, H, N, d, o, o_bf16, lse, stream):
@@ -238,17 +257,20 @@ def _check_bf16(**tensors):
 
 def forward_fp8(q, k, vt, q_descale, k_descale, v_descale, *, scale=None, causal=False, key_lens=None,
                 stream=None):
-    """FP8 forward: q [B, H, N, d], k [B, Hkv, N, d], vt [B, Hkv, d, N] (V
-    transposed) as torch.float8_e4m3fn GPU tensors standing for descale ·
-    stored value.  Returns (o bf16 [B, H, N, d], lse fp32 [B, H, N])."""
+    """FP8 forward: q [B, H, N, d], k [B, Hkv, N, d], vt [B, Hkv, d, N16] (V
+    transposed, N16 = N rounded up to a multiple of 16) as
+    torch.float8_e4m3fn GPU tensors standing for descale · stored value.
+    Returns (o bf16 [B, H, N, d], lse fp32 [B, H, N])."""
     import torch
 
     if q.dim() != 4 or k.dim() != 4 or vt.dim() != 4:
         raise ValueError("q, k, vt must be 4-D")
     B, H, N, d = q.shape
     Hkv = k.shape[1]
-    if tuple(k.shape) != (B, Hkv, N, d) or tuple(vt.shape) != (B, Hkv, d, N):
-        raise ValueError("shape mismatch: k must be [B, Hkv, N, d] and vt [B, Hkv, d, N]")
+    n16 = (N + 15) // 16 * 16
+    if tuple(k.shape) != (B, Hkv, N, d) or tuple(vt.shape) != (B, Hkv, d, n16):
+        raise ValueError("shape mismatch: k must be [B, Hkv, N, d] and vt [B, Hkv, d, N16] (N16 = N rounded up "
+                         "to a multiple of 16)")
     for name, t in (("q", q), ("k", k), ("vt", vt)):
         if t.dtype != torch.float8_e4m3fn or not t.is_cuda or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous float8_e4m3fn GPU tensor")
@@ -268,6 +290,70 @@ def forward_fp8(q, k, vt, q_descale, k_descale, v_descale, *, scale=None, causal
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd_fp8")
     return o, lse
+
+
+def hadamard_signs(d, seed, device):
+    """d random signs (+1 / -1, fp32) for the incoherent-processing rotation,
+    drawn on the CPU by a torch.Generator seeded with ``seed`` and copied to
+    ``device``."""
+    import torch
+
+    g = torch.Generator("cpu").manual_seed(int(seed))
+    s = torch.randint(0, 2, (d,), generator=g, dtype=torch.int32).float() * 2.0 - 1.0
+    return s.to(device)
+
+
+def quantize_fp8(x, signs=None, *, stream=None):
+    """Per-tensor fp8 e4m3 quantisation of a bf16 GPU tensor [..., d] on the
+    GPU (attn_fp8_amax, then attn_fp8_quantize), each row first rotated by
+    R = H_d · diag(signs) / sqrt(d) when ``signs`` (fp32 GPU tensor [d]) is
+    given.  Returns (x8 float8_e4m3fn like x, descale float).  Reading the
+    descale back waits for the two kernels."""
+    import torch
+
+    _check_bf16(x=x)
+    d = x.shape[-1]
+    rows = x.numel() // d if d else 0
+    if signs is not None and (signs.dtype != torch.float32 or not signs.is_cuda or signs.numel() != d
+                              or not signs.is_contiguous()):
+        raise ValueError("signs must be a contiguous float32 GPU tensor with d entries")
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    scal = torch.empty(8, dtype=torch.float32, device=x.device)  # [0] amax, [4] descale (16-byte apart)
+    x8 = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=x.device)
+    sp = signs.data_ptr() if signs is not None else None
+    st = attn_fp8_amax(x.data_ptr(), sp, rows, d, scal.data_ptr(), stream)
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fp8_amax")
+    st = attn_fp8_quantize(x.data_ptr(), sp, rows, d, scal.data_ptr(), x8.data_ptr(), scal[4:].data_ptr(), stream)
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fp8_quantize")
+    return x8, float(scal[4].item())
+
+
+def quantize_fp8_vt(v, *, stream=None):
+    """V [B, Hkv, N, d] bf16 (GPU) to its transposed fp8 form for forward_fp8:
+    (vt8 float8_e4m3fn [B, Hkv, d, N16], descale float), per-tensor scale,
+    on the GPU (attn_fp8_amax, then attn_fp8_quantize_vt)."""
+    import torch
+
+    _check_bf16(v=v)
+    if v.dim() != 4:
+        raise ValueError("v must be [B, Hkv, N, d]")
+    B, Hkv, N, d = v.shape
+    n16 = (N + 15) // 16 * 16
+    if stream is None:
+        stream = torch.cuda.current_stream(v.device).cuda_stream
+    scal = torch.empty(8, dtype=torch.float32, device=v.device)
+    vt8 = torch.empty((B, Hkv, d, n16), dtype=torch.float8_e4m3fn, device=v.device)
+    st = attn_fp8_amax(v.data_ptr(), None, B * Hkv * N, d, scal.data_ptr(), stream)
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fp8_amax")
+    st = attn_fp8_quantize_vt(v.data_ptr(), B * Hkv, N, d, scal.data_ptr(), vt8.data_ptr(), scal[4:].data_ptr(),
+                              stream)
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fp8_quantize_vt")
+    return vt8, float(scal[4].item())
 
 
 def forward_partial(q, k, v, *, q_offset=0, k_offset=0, scale=None, causal=False, stream=None):

@@ -11,7 +11,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libattn.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
-SOURCES = ["attn_api.hip", "attn_fwd_bf16.hip", "attn_fwd_f32.hip", "attn_bwd_bf16.hip", "attn_merge.hip", "attn_fwd_fp8.hip"]
+SOURCES = ["attn_api.hip", "attn_fwd_bf16.hip", "attn_fwd_f32.hip", "attn_bwd_bf16.hip", "attn_merge.hip", "attn_fwd_fp8.hip",
+           "attn_fp8_prep.hip"]
 
 # Packed fp32 VALU forms (v_pk_add_f32, v_pk_mul_f32, v_pk_fma_f32) are
 # turned off for the device code: without the feature flag the compiler pairs

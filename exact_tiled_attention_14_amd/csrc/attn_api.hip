@@ -19,6 +19,11 @@ hipError_t launch_merge(const float* o_parts, const float* lse_parts, int S, int
                         bool o_bf16, float* lse, hipStream_t stream);
 hipError_t launch_merge_bf16_parts(const uint16_t* o_parts, const float* lse_parts, int S, int64_t rows, int d,
                                    void* o, float* lse, hipStream_t stream);
+hipError_t launch_fp8_amax(const void* x, const float* signs, int64_t rows, int d, float* amax, hipStream_t stream);
+hipError_t launch_fp8_quantize(const void* x, const float* signs, int64_t rows, int d, const float* amax, void* x8,
+                               float* descale, hipStream_t stream);
+hipError_t launch_fp8_quantize_vt(const void* v, int64_t heads, int N, int d, const float* amax, void* vt8,
+                                  float* descale, hipStream_t stream);
 }  // namespace attn
 
 namespace {
@@ -300,7 +305,6 @@ int attn_fwd_fp8(const void* q, const void* k, const void* vt, void* o, float* l
                  float q_descale, float k_descale, float v_descale,
                  int B, int H, int Hkv, int N, int d, float scale, int causal,
                  const int32_t* key_lens, void* stream) {
-    if (N >= 0 && N % 16 != 0) return ATTN_ERR_SHAPE;  // Vᵀ rows are read in 16-byte pieces
     if (!isfinite(q_descale) || !isfinite(k_descale) || !isfinite(v_descale)) return ATTN_ERR_SCALE;
     attn::Params p;
     bool empty = false;
@@ -310,9 +314,58 @@ int attn_fwd_fp8(const void* q, const void* k, const void* vt, void* o, float* l
                             &p, &empty);
     if (st != ATTN_OK || empty) return st;
     p.o_scale = v_descale;
+    p.Nk = (N + 15) / 16 * 16;  // Vᵀ row length: keys rounded up to whole 16-byte pieces
     (void)hipGetLastError();
     const hipError_t e = attn::launch_fwd_fp8(p, d, causal != 0, static_cast<hipStream_t>(stream));
     return hip_status(e);
+}
+
+namespace {
+// rows of d values must be addressable: rows·d bytes of fp8 and twice that of bf16
+constexpr int64_t kMaxPrepRows = ((int64_t)1 << 46);
+}  // namespace
+
+int attn_fp8_amax(const void* x, const float* signs, int64_t rows, int d, float* amax, void* stream) {
+    if (rows < 0 || rows > kMaxPrepRows) return ATTN_ERR_SHAPE;
+    if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
+    if (!amax || (rows > 0 && !x)) return ATTN_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(amax) & 3u) != 0 || (x && !aligned16(x)) || (signs && !aligned16(signs)))
+        return ATTN_ERR_ALIGN;
+    (void)hipGetLastError();
+    return hip_status(attn::launch_fp8_amax(x, signs, rows, d, amax, static_cast<hipStream_t>(stream)));
+}
+
+int attn_fp8_quantize(const void* x, const float* signs, int64_t rows, int d, const float* amax, void* x8,
+                      float* descale, void* stream) {
+    if (rows < 0 || rows > kMaxPrepRows) return ATTN_ERR_SHAPE;
+    if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
+    if (!amax || !descale || (rows > 0 && (!x || !x8))) return ATTN_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(amax) & 3u) != 0 || (reinterpret_cast<uintptr_t>(descale) & 3u) != 0 ||
+        (x && !aligned16(x)) || (x8 && !aligned16(x8)) || (signs && !aligned16(signs)))
+        return ATTN_ERR_ALIGN;
+    (void)hipGetLastError();
+    return hip_status(
+        attn::launch_fp8_quantize(x, signs, rows, d, amax, x8, descale, static_cast<hipStream_t>(stream)));
+}
+
+int attn_fp8_quantize_vt(const void* v, int64_t heads, int N, int d, const float* amax, void* vt8, float* descale,
+                         void* stream) {
+    if (heads < 0 || N < 0 || heads * (((int64_t)N + 63) / 64) >= ((int64_t)1 << 31) ||
+        (int64_t)N * d * 2 >= ((int64_t)1 << 31))
+        return ATTN_ERR_SHAPE;
+    if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
+    if (!amax || !descale || (heads > 0 && N > 0 && (!v || !vt8))) return ATTN_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(amax) & 3u) != 0 || (reinterpret_cast<uintptr_t>(descale) & 3u) != 0 ||
+        (v && !aligned16(v)) || (vt8 && !aligned16(vt8)))
+        return ATTN_ERR_ALIGN;
+    if (heads == 0 || N == 0) {  // nothing to convert; the descale is still written
+        (void)hipGetLastError();
+        return hip_status(attn::launch_fp8_quantize(nullptr, nullptr, 0, d, amax, nullptr, descale,
+                                                    static_cast<hipStream_t>(stream)));
+    }
+    (void)hipGetLastError();
+    return hip_status(
+        attn::launch_fp8_quantize_vt(v, heads, N, d, amax, vt8, descale, static_cast<hipStream_t>(stream)));
 }
 
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,

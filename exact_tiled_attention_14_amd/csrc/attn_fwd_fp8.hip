@@ -5,7 +5,8 @@
 //
 // Inputs are fp8 tensors with one fp32 descale factor each (value =
 // descale · stored fp8): q, k row-major [.., N, d], V given transposed
-// ([.., d, N]) so that both matrix-core operands of O = P·V run along the key
+// ([.., d, N16], N16 = N rounded up to a multiple of 16, the columns past N
+// unused) so that both matrix-core operands of O = P·V run along the key
 // axis.  Per 64-key tile and wave (32 query rows, as in the bf16 kernel):
 //
 //   Sᵀ = K·Qᵀ        2 (d = 64) or 4 (d = 128) MFMAs of 32 keys × 32 rows × 64 d
@@ -192,11 +193,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_fp8_kernel(Params p) {
 
     const uint8_t* qp = static_cast<const uint8_t*>(p.q) + (size_t)(t.b * p.H + t.h) * p.N * D;
     const uint8_t* kb = static_cast<const uint8_t*>(p.k) + (size_t)(t.b * p.Hkv + g) * p.N * D;
-    const uint8_t* vt = static_cast<const uint8_t*>(p.v) + (size_t)(t.b * p.Hkv + g) * D * p.N;
+    // Vᵀ rows hold p.Nk bytes: the N keys rounded up to whole 16-byte pieces
+    const uint8_t* vt = static_cast<const uint8_t*>(p.v) + (size_t)(t.b * p.Hkv + g) * D * p.Nk;
 
     Offsets8<D> o;
-    o.init(wave, lane, p.N);
-    load_tile8<D>(o, s0, spare, kb, vt, 0, ntiles > 0 ? kv_len : 0, p.N, wave);
+    o.init(wave, lane, p.Nk);
+    load_tile8<D>(o, s0, spare, kb, vt, 0, ntiles > 0 ? kv_len : 0, p.Nk, wave);
 
     // Q rows as the Sᵀ B operand: chunk c holds d = 64c + 32h .. + 31
     i32x8 qf[C::DC];
@@ -222,12 +224,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_fp8_kernel(Params p) {
     float m_run = kNegInf, l_run = 0.f;
     const float c2 = p.scale_log2;
 
-    load_tile8<D>(o, s1, spare, kb, vt, BC, ntiles > 1 ? kv_len : 0, p.N, wave);
+    load_tile8<D>(o, s1, spare, kb, vt, BC, ntiles > 1 ? kv_len : 0, p.Nk, wave);
     wait_older_and_sync<D>();  // tile 0 (and Q) in; tile 1 may still be on its way
 
     auto step = [&](int j, const char* cur, char* next2) __attribute__((always_inline)) {
         const int kv0 = j * BC;
-        load_tile8<D>(o, next2, spare, kb, vt, kv0 + 2 * BC, j + 2 < ntiles ? kv_len : 0, p.N, wave);
+        load_tile8<D>(o, next2, spare, kb, vt, kv0 + 2 * BC, j + 2 < ntiles ? kv_len : 0, p.Nk, wave);
         if (!(CAUSAL && kv0 > q0w + 31)) {  // (a wave whose rows all precede the tile skips it)
             const bool masked = (kv0 + BC > kv_len) || (CAUSAL && kv0 + BC - 1 > q0w);
             f32x16 s[2];

@@ -99,22 +99,66 @@ int attn_fwd_varlen_bf16(const void* q, const void* k, const void* v, void* o, f
 
 /* FP8 forward (the low-precision step of the unite.ai page, section
  * "闪电注意力-3"): the operation above on fp8 operands.  q [B][H][N][d],
- * k [B][Hkv][N][d] and vt [B][Hkv][d][N] (V TRANSPOSED: its rows are the d
- * features, each over the N keys) hold OCP fp8 e4m3 bytes; the values they
- * stand for are q_descale·q, k_descale·k, v_descale·v.  Outputs o bf16
- * [B][H][N][d] and lse fp32 [B][H][N] as for attn_fwd_bf16, for those values.
- * Both products run on fp8 matrix cores with fp32 accumulation; the softmax
- * runs in fp32 and its weights are rounded to fp8 e4m3 (relative error at
- * most 2^-4 each, after scaling by 2^7 relative to a running reference that
- * is at most 2x below the true max, so they stay in range) before P·V; the
- * row sums use the fp32 weights.  N must be a multiple of 16; descale
- * factors finite; scale·q_descale·k_descale finite.  Other limits, checks
- * and status codes as attn_fwd_bf16 (vt is checked as its v).  Padded keys
- * (past key_lens[b]) never reach the output, NaN included. */
+ * k [B][Hkv][N][d] and vt [B][Hkv][d][N16] (V TRANSPOSED: its rows are the d
+ * features, each over the keys; N16 = N rounded up to a multiple of 16, and
+ * the columns N .. N16 - 1 of a row are never used) hold OCP fp8 e4m3 bytes;
+ * the values they stand for are q_descale·q, k_descale·k, v_descale·v.
+ * Outputs o bf16 [B][H][N][d] and lse fp32 [B][H][N] as for attn_fwd_bf16,
+ * for those values.  Both products run on fp8 matrix cores with fp32
+ * accumulation; the softmax runs in fp32 and its weights are rounded to fp8
+ * e4m3 (relative error at most 2^-4 each, after scaling by 2^7 relative to a
+ * running reference that is at most 2x below the true max, so they stay in
+ * range) before P·V; the row sums use the fp32 weights.  Any N >= 0;
+ * descale factors finite; scale·q_descale·k_descale finite.  Other limits,
+ * checks and status codes as attn_fwd_bf16 (vt is checked as its v).  Padded
+ * keys (past key_lens[b]) never reach the output, NaN included.  The inputs
+ * can be made on the GPU with attn_fp8_amax, attn_fp8_quantize (queries and
+ * keys, optionally rotated: incoherent processing) and attn_fp8_quantize_vt. */
 int attn_fwd_fp8(const void* q, const void* k, const void* vt, void* o, float* lse,
                  float q_descale, float k_descale, float v_descale,
                  int B, int H, int Hkv, int N, int d, float scale, int causal,
                  const int32_t* key_lens, void* stream);
+
+/* Incoherent processing and fp8 quantisation (unite.ai page, section
+ * "闪电注意力-3": FlashAttention-3 uses incoherent processing to lower the
+ * quantisation error of its FP8 step).  The rotation R = H_d · diag(signs)
+ * / sqrt(d) (H_d the Sylvester-Hadamard matrix, H[i][j] =
+ * (-1)^popcount(i & j); signs a caller-drawn fp32 vector of d values +1 or
+ * -1) multiplies every row of q and of k: applied to both with the same
+ * signs it leaves every score q·k, and so O and LSE, unchanged, while an
+ * outlier feature is spread over all d features before the per-tensor scale
+ * is chosen.  V is not rotated.
+ *
+ * attn_fp8_amax: *amax = the largest |R x| over the `rows` rows of d bf16
+ * values of x ([rows][d], contiguous); signs == NULL: the largest |x| (no
+ * rotation).  NaN entries take no part.  amax is a DEVICE float, first set
+ * to 0 and then raised with atomic maxima (two kernels on `stream`).
+ *
+ * attn_fp8_quantize: x8[r][:] = e4m3(R x[r] / descale) (or x[r] / descale
+ * when signs is NULL), e4m3 meaning OCP fp8 E4M3FN, nearest value, ties to
+ * even, after clamping to +-448 (NaN stays NaN), with descale = *amax / 448
+ * in fp32 (1 when *amax is 0); the kernel also writes that descale into the
+ * DEVICE float *descale, the value attn_fwd_fp8 needs for this tensor.  x8
+ * is [rows][d] bytes.
+ *
+ * attn_fp8_quantize_vt: V [heads][N][d] bf16 (heads = B·Hkv) to its
+ * transposed fp8 form vt8 [heads][d][N16] (N16 = N rounded up to a multiple
+ * of 16, columns N .. N16 - 1 written as 0), e4m3(v / descale) with descale
+ * from *amax as above (use attn_fp8_amax with signs == NULL on v first),
+ * also written to *descale.
+ *
+ * All pointers are DEVICE pointers: x, x8, v, vt8 and signs 16-byte aligned,
+ * amax and descale 4-byte aligned; outputs must not overlap inputs.  rows >=
+ * 0 (at most 2^46), heads >= 0, N >= 0 (N·d·2 below 2^31), d in {64, 128}.
+ * Status codes: ATTN_ERR_SHAPE, ATTN_ERR_HEAD_DIM, ATTN_ERR_NULL,
+ * ATTN_ERR_ALIGN (checked in that order, before any HIP call), ATTN_ERR_HIP.
+ * Enqueued on `stream`, not waited on.  These kernels are bound by HBM (2
+ * bytes read and 1 written per element). */
+int attn_fp8_amax(const void* x, const float* signs, int64_t rows, int d, float* amax, void* stream);
+int attn_fp8_quantize(const void* x, const float* signs, int64_t rows, int d, const float* amax, void* x8,
+                      float* descale, void* stream);
+int attn_fp8_quantize_vt(const void* v, int64_t heads, int N, int d, const float* amax, void* vt8, float* descale,
+                         void* stream);
 
 /* Split-KV (the key range of every query cut into pieces whose partial
  * results are combined afterwards: the softmax-merge rule of the unite.ai

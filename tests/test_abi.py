@@ -296,7 +296,7 @@ def call_fp8(**over):
 
 
 @pytest.mark.parametrize("over,status", [
-    (dict(N=60), attn.ATTN_ERR_SHAPE),           # V transposed is read in 16-byte pieces
+    (dict(N=-1), attn.ATTN_ERR_SHAPE),
     (dict(d=96), attn.ATTN_ERR_HEAD_DIM),
     (dict(qd=math.nan), attn.ATTN_ERR_SCALE),
     (dict(vd=math.inf), attn.ATTN_ERR_SCALE),
@@ -309,6 +309,33 @@ def call_fp8(**over):
 ])
 def test_fp8_host_validation(over, status):
     assert call_fp8(**over) == status
+
+
+@pytest.mark.parametrize("call,status", [
+    # attn_fp8_amax(x, signs, rows, d, amax, stream)
+    (lambda: attn.attn_fp8_amax(P, None, -1, 64, P, None), attn.ATTN_ERR_SHAPE),
+    (lambda: attn.attn_fp8_amax(P, None, 1 << 47, 64, P, None), attn.ATTN_ERR_SHAPE),
+    (lambda: attn.attn_fp8_amax(P, None, 4, 96, P, None), attn.ATTN_ERR_HEAD_DIM),
+    (lambda: attn.attn_fp8_amax(P, None, 4, 64, None, None), attn.ATTN_ERR_NULL),
+    (lambda: attn.attn_fp8_amax(None, None, 4, 64, P, None), attn.ATTN_ERR_NULL),
+    (lambda: attn.attn_fp8_amax(P + 8, None, 4, 64, P, None), attn.ATTN_ERR_ALIGN),
+    (lambda: attn.attn_fp8_amax(P, P + 4, 4, 64, P, None), attn.ATTN_ERR_ALIGN),
+    (lambda: attn.attn_fp8_amax(P, None, 4, 64, P + 2, None), attn.ATTN_ERR_ALIGN),
+    # attn_fp8_quantize(x, signs, rows, d, amax, x8, descale, stream)
+    (lambda: attn.attn_fp8_quantize(P, None, -5, 128, P, P, P, None), attn.ATTN_ERR_SHAPE),
+    (lambda: attn.attn_fp8_quantize(P, None, 4, 32, P, P, P, None), attn.ATTN_ERR_HEAD_DIM),
+    (lambda: attn.attn_fp8_quantize(P, None, 4, 128, P, None, P, None), attn.ATTN_ERR_NULL),
+    (lambda: attn.attn_fp8_quantize(P, None, 4, 128, P, P, None, None), attn.ATTN_ERR_NULL),
+    (lambda: attn.attn_fp8_quantize(P, None, 4, 128, P, P + 8, P, None), attn.ATTN_ERR_ALIGN),
+    # attn_fp8_quantize_vt(v, heads, N, d, amax, vt8, descale, stream)
+    (lambda: attn.attn_fp8_quantize_vt(P, -1, 64, 64, P, P, P, None), attn.ATTN_ERR_SHAPE),
+    (lambda: attn.attn_fp8_quantize_vt(P, 2, -1, 64, P, P, P, None), attn.ATTN_ERR_SHAPE),
+    (lambda: attn.attn_fp8_quantize_vt(P, 2, 64, 100, P, P, P, None), attn.ATTN_ERR_HEAD_DIM),
+    (lambda: attn.attn_fp8_quantize_vt(None, 2, 64, 64, P, P, P, None), attn.ATTN_ERR_NULL),
+    (lambda: attn.attn_fp8_quantize_vt(P, 2, 64, 64, P, P + 4, P, None), attn.ATTN_ERR_ALIGN),
+])
+def test_fp8_prep_host_validation(call, status):
+    assert call() == status
 
 
 def test_fp8_quantisation_recipe():

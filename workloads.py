@@ -140,8 +140,8 @@ def quantize_fp8(x):
 def make_fp8(B, H, Hkv, N, d, seed=0, padded=False):
     """fp8 inputs following the recipe above: q, k, v drawn as for
     ``make_qkv`` (fp32 N(0, 1)), each quantised per tensor with
-    ``quantize_fp8``; V is also returned transposed ([B, Hkv, d, N]) as the
-    fp8 path takes it.  Returns (q8, k8, v8, vt8, (qd, kd, vd), key_lens)."""
+    ``quantize_fp8``; V is also returned transposed ([B, Hkv, d, N16], see
+    ``transpose_fp8_v``) as the fp8 path takes it.  Returns (q8, k8, v8, vt8, (qd, kd, vd), key_lens)."""
     g = torch.Generator("cpu").manual_seed(int(seed))
     q = torch.randn((B, H, N, d), generator=g, dtype=torch.float32)
     k = torch.randn((B, Hkv, N, d), generator=g, dtype=torch.float32)
@@ -152,5 +152,15 @@ def make_fp8(B, H, Hkv, N, d, seed=0, padded=False):
     q8, qd = quantize_fp8(q)
     k8, kd = quantize_fp8(k)
     v8, vd = quantize_fp8(v)
-    vt8 = v8.transpose(-1, -2).contiguous()
-    return q8, k8, v8, vt8, (qd, kd, vd), key_lens
+    return q8, k8, v8, transpose_fp8_v(v8), (qd, kd, vd), key_lens
+
+
+def transpose_fp8_v(v8):
+    """V [B, Hkv, N, d] (fp8) in the fp8 path's transposed layout
+    [B, Hkv, d, N16], N16 = N rounded up to a multiple of 16, the extra columns
+    zero."""
+    B, Hkv, N, d = v8.shape
+    n16 = (N + 15) // 16 * 16
+    vt = torch.zeros((B, Hkv, d, n16), dtype=torch.uint8)
+    vt[..., :N] = v8.view(torch.uint8).transpose(-1, -2)
+    return vt.view(torch.float8_e4m3fn)
