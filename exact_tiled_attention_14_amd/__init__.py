@@ -26,11 +26,12 @@ __all__ = [
     "attn_status_str", "forward", "forward_varlen", "forward_partial", "merge", "forward_splitkv", "backward",
     "library_path", "load_library", "ATTN_ERR_WORKSPACE", "ATTN_MAX_SPLITS",
     "ATTN_OK", "ATTN_ERR_NULL", "ATTN_ERR_SHAPE", "ATTN_ERR_HEAD_DIM", "ATTN_ERR_ALIGN",
-    "ATTN_ERR_SCALE", "ATTN_ERR_HIP",
+    "ATTN_ERR_SCALE", "ATTN_ERR_HIP", "ATTN_ERR_SCRATCH", "ATTN_NOALLOC_SCRATCH_FLOATS", "attn_bwd_bf16_noalloc",
 ]
 
 ATTN_OK, ATTN_ERR_NULL, ATTN_ERR_SHAPE, ATTN_ERR_HEAD_DIM = 0, 1, 2, 3
-ATTN_ERR_ALIGN, ATTN_ERR_SCALE, ATTN_ERR_HIP, ATTN_ERR_WORKSPACE = 4, 5, 6, 7
+ATTN_ERR_ALIGN, ATTN_ERR_SCALE, ATTN_ERR_HIP, ATTN_ERR_WORKSPACE, ATTN_ERR_SCRATCH = 4, 5, 6, 7, 8
+ATTN_NOALLOC_SCRATCH_FLOATS = 4 * 1024 * 1024
 ATTN_MAX_SPLITS = 64
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -52,6 +53,7 @@ ENTRY_POINTS = {
     "attn_splitkv_workspace_bytes": ([_I] * 5, ctypes.c_size_t),
     "attn_fwd_fp8": ([_P] * 5 + [ctypes.c_float] * 3 + [_I] * 5 + [ctypes.c_float, _I, _P, _P], ctypes.c_int),
     "attn_bwd_bf16": ([_P] * 10 + [_I, _I, _I, _I, _I, ctypes.c_float, _I, _P, _P], ctypes.c_int),
+    "attn_bwd_bf16_noalloc": ([_P] * 9 + [_I, _I, _I, _I, _I, ctypes.c_float, _I, _P, _P], ctypes.c_int),
     "attn_fp8_amax": ([_P, _P, ctypes.c_int64, _I, _P, _P], ctypes.c_int),
     "attn_fp8_quantize": ([_P, _P, ctypes.c_int64, _I, _P, _P, _P, _P], ctypes.c_int),
     "attn_fp8_quantize_vt": ([_P, ctypes.c_int64, _I, _I, _P, _P, _P, _P], ctypes.c_int),
@@ -158,6 +160,11 @@ def attn_splitkv_workspace_bytes(B, H, N, d, num_splits):
 def attn_bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, delta, B, H, Hkv, N, d, scale, causal, key_lens, stream):
     return load_library().attn_bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, delta,
                                         B, H, Hkv, N, d, scale, causal, key_lens, stream)
+
+
+def attn_bwd_bf16_noalloc(q, k, v, o, dout, lse, dq, dk, dv, B, H, Hkv, N, d, scale, causal, key_lens, stream):
+    return load_library().attn_bwd_bf16_noalloc(q, k, v, o, dout, lse, dq, dk, dv,
+                                                B, H, Hkv, N, d, scale, causal, key_lens, stream)
 
 
 def attn_status_str(status):
@@ -444,11 +451,15 @@ def forward_splitkv(q, k, v, num_splits, *, q_offset=0, k_offset=0, scale=None, 
     return o, lse
 
 
-def backward(q, k, v, o, lse, dout, *, scale=None, causal=False, key_lens=None, stream=None):
+def backward(q, k, v, o, lse, dout, *, scale=None, causal=False, key_lens=None, stream=None, out=None,
+             builtin_scratch=False):
     """Gradients (dq, dk, dv) of sum(o * dout) for bf16 GPU tensors, where
     (o, lse) = forward(q, k, v, ...) with the same arguments.  Allocates the
-    outputs and the fp32 [B, H, N] D buffer; the two kernels are enqueued on
-    ``stream`` (default: torch's current stream) and not waited on."""
+    outputs (unless ``out`` = (dq, dk, dv) is given) and the fp32 [2, B, H, N]
+    scratch; with ``builtin_scratch`` it calls attn_bwd_bf16_noalloc instead,
+    whose scratch is built into the library, so that with ``out`` given
+    nothing is allocated.  The two kernels are enqueued on ``stream``
+    (default: torch's current stream) and not waited on."""
     import torch
 
     B, H, N, d = q.shape
@@ -465,16 +476,27 @@ def backward(q, k, v, o, lse, dout, *, scale=None, causal=False, key_lens=None, 
         key_lens = key_lens.contiguous()
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    dq = torch.empty_like(q)
-    dk = torch.empty_like(k)
-    dv = torch.empty_like(v)
-    delta = torch.empty((2, B, H, N), dtype=torch.float32, device=q.device)
+    if out is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    else:
+        dq, dk, dv = out
+        for name, t, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+            if t.shape != like.shape or t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous bfloat16 GPU tensor shaped like its input")
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
+    kl = key_lens.data_ptr() if key_lens is not None else None
+    if builtin_scratch:
+        st = attn_bwd_bf16_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                                   lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                   B, H, Hkv, N, d, float(scale), int(bool(causal)), kl, stream)
+        if st != ATTN_OK:
+            raise AttnError(st, "attn_bwd_bf16_noalloc")
+        return dq, dk, dv
+    delta = torch.empty((2, B, H, N), dtype=torch.float32, device=q.device)
     st = attn_bwd_bf16(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
                        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
-                       B, H, Hkv, N, d, float(scale), int(bool(causal)),
-                       key_lens.data_ptr() if key_lens is not None else None, stream)
+                       B, H, Hkv, N, d, float(scale), int(bool(causal)), kl, stream)
     if st != ATTN_OK:
         raise AttnError(st, "attn_bwd_bf16")
     return dq, dk, dv

@@ -176,6 +176,69 @@ int attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o, co
     return hip_status(e);
 }
 
+namespace {
+
+// The backward entry point that allocates nothing keeps its D / base-2 LSE
+// scratch (2·B·H·N floats) in this array: each GPU the library runs on holds
+// its own copy, at its own address, until the process ends.  In host code the
+// name is only a stand-in for the device array, so kernels get the address
+// from hipGetSymbolAddress (looked up once per device, with that device
+// current) and never the name.
+static __device__ __align__(256) float scratch[ATTN_NOALLOC_SCRATCH_FLOATS];
+
+// Device address of `scratch` on the current device; NULL (and *err set) if
+// the lookup fails.  Concurrent first calls on one device look it up twice
+// and store the same address.
+float* scratch_ptr(hipError_t* err) {
+    static std::atomic<float*> cached[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= 64) {
+        *err = e != hipSuccess ? e : hipErrorInvalidDevice;
+        return nullptr;
+    }
+    float* ptr = cached[dev].load(std::memory_order_acquire);
+    if (ptr == nullptr) {
+        void* addr = nullptr;
+        e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || addr == nullptr) {
+            *err = e != hipSuccess ? e : hipErrorInvalidSymbol;
+            return nullptr;
+        }
+        ptr = static_cast<float*>(addr);
+        cached[dev].store(ptr, std::memory_order_release);
+    }
+    return ptr;
+}
+
+}  // namespace
+
+int attn_bwd_bf16_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                          const float* lse, void* dq, void* dk, void* dv,
+                          int B, int H, int Hkv, int N, int d, float scale, int causal,
+                          const int32_t* key_lens, void* stream) {
+    attn::BwdParams bp;
+    bool empty = false;
+    const int st = validate(q, k, v, dq, lse, B, H, Hkv, N, d, scale, causal, key_lens, &bp.f, &empty);
+    if (st != ATTN_OK || empty) return st;
+    if (!o || !dout || !dk || !dv) return ATTN_ERR_NULL;
+    if (!aligned16(o) || !aligned16(dout) || !aligned16(dk) || !aligned16(dv)) return ATTN_ERR_ALIGN;
+    if (2 * (int64_t)B * H * N > (int64_t)ATTN_NOALLOC_SCRATCH_FLOATS) return ATTN_ERR_SCRATCH;
+    (void)hipGetLastError();
+    hipError_t e = hipSuccess;
+    float* delta = scratch_ptr(&e);
+    if (delta == nullptr) return hip_status(e);
+    bp.o = o;
+    bp.dout = dout;
+    bp.dq = dq;
+    bp.dk = dk;
+    bp.dv = dv;
+    bp.delta = delta;  // fully written by the first kernel before the second reads it
+    bp.scale = scale;
+    e = attn::launch_bwd_bf16(bp, d, causal != 0, static_cast<hipStream_t>(stream));
+    return hip_status(e);
+}
+
 int attn_fwd_varlen_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                          const int32_t* cu_seqlens, int B, int H, int Hkv, int total, int max_seqlen,
                          int d, float scale, int causal, void* stream) {
@@ -392,6 +455,9 @@ const char* attn_status_str(int status) {
         case ATTN_ERR_SCALE: return "scale must be finite";
         case ATTN_ERR_HIP: return "HIP kernel launch failed";
         case ATTN_ERR_WORKSPACE: return "workspace missing or smaller than attn_splitkv_workspace_bytes";
+        case ATTN_ERR_SCRATCH:
+            return "the problem needs more than the built-in scratch (attn_bwd_bf16_noalloc: 2*B*H*N floats must not "
+                   "exceed ATTN_NOALLOC_SCRATCH_FLOATS)";
         default: return "unknown attn status";
     }
 }

@@ -56,8 +56,12 @@ typedef enum {
     ATTN_ERR_ALIGN = 4,     /* a pointer is not 16-byte aligned                   */
     ATTN_ERR_SCALE = 5,     /* scale is NaN or infinite                           */
     ATTN_ERR_HIP = 6,       /* the kernel launch failed (hipGetLastError)         */
-    ATTN_ERR_WORKSPACE = 7  /* split-KV workspace NULL or too small               */
+    ATTN_ERR_WORKSPACE = 7, /* split-KV workspace NULL or too small               */
+    ATTN_ERR_SCRATCH = 8    /* larger than the built-in scratch of a no-alloc call */
 } attn_status;
+
+/* Floats of the built-in device scratch of attn_bwd_bf16_noalloc (16 MiB). */
+#define ATTN_NOALLOC_SCRATCH_FLOATS (4 * 1024 * 1024)
 
 /* Most key ranges one split-KV call may use. */
 #define ATTN_MAX_SPLITS 64
@@ -236,6 +240,25 @@ int attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o, co
                   void* dq, void* dk, void* dv, float* delta,
                   int B, int H, int Hkv, int N, int d, float scale, int causal,
                   const int32_t* key_lens, void* stream);
+
+/* attn_bwd_bf16 for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight training loops, harnesses that forbid hipMalloc):
+ * the same arguments without `delta`, the same kernels and results.  The D /
+ * base-2 LSE scratch (2·B·H·N floats) lives in a device array built into the
+ * library, ATTN_NOALLOC_SCRATCH_FLOATS floats (16 MiB) on each GPU the
+ * library runs on, held until the process ends; a problem with 2·B·H·N above
+ * that limit returns ATTN_ERR_SCRATCH (checked on the host after the checks
+ * of attn_bwd_bf16, before any HIP call).  The call allocates nothing: no
+ * hipMalloc, no hipFree, no allocating library routine.  The first call on a
+ * device looks up the array's address there (hipGetSymbolAddress).  Every
+ * call on one GPU shares that GPU's array, so calls that overlap on one GPU
+ * (concurrent streams, or threads on one stream) race and give undefined
+ * results; calls in stream order do not.  Nothing needs clearing between
+ * calls: the first kernel writes every scratch value the second reads. */
+int attn_bwd_bf16_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                          const float* lse, void* dq, void* dk, void* dv,
+                          int B, int H, int Hkv, int N, int d, float scale, int causal,
+                          const int32_t* key_lens, void* stream);
 
 /* The hot path: identical to attn_fwd_bf16. */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,

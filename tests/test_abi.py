@@ -338,6 +338,30 @@ def test_fp8_prep_host_validation(call, status):
     assert call() == status
 
 
+def test_noalloc_backward_host_validation():
+    """attn_bwd_bf16_noalloc: the checks of attn_bwd_bf16, then the size of
+    the built-in scratch (2·B·H·N floats), all before any HIP call."""
+    f = attn.attn_bwd_bf16_noalloc
+    args = [P] * 9 + [1, 2, 1, 64, 64, 0.125, 0, None, None]
+
+    def call(**kw):
+        a = list(args)
+        names = ["q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv", "B", "H", "Hkv", "N", "d"]
+        for key, val in kw.items():
+            a[names.index(key)] = val
+        return f(*a)
+
+    assert call(d=96) == attn.ATTN_ERR_HEAD_DIM
+    assert call(H=3, Hkv=2) == attn.ATTN_ERR_SHAPE
+    assert call(dout=None) == attn.ATTN_ERR_NULL
+    assert call(dv=P + 4) == attn.ATTN_ERR_ALIGN
+    assert call(B=0) == attn.ATTN_OK
+    limit = attn.ATTN_NOALLOC_SCRATCH_FLOATS
+    assert call(B=1, H=1, N=limit // 2 + 1) == attn.ATTN_ERR_SCRATCH
+    assert call(B=4, H=32, N=limit // 256 + 1) == attn.ATTN_ERR_SCRATCH
+    assert attn.ATTN_ERR_SCRATCH == 8 and "scratch" in attn.attn_status_str(attn.ATTN_ERR_SCRATCH)
+
+
 def test_fp8_quantisation_recipe():
     """The test-input quantiser: values within half an e4m3 step, no NaN
     from out-of-range magnitudes, max maps to 448."""
