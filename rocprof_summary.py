@@ -16,11 +16,11 @@ output directory):
         python3 bench.py --copy-calibration 512          (and WRITE_SIZE)
     rocprofv3 --pmc FETCH_SIZE -d OUT/tr_FETCH_SIZE_W -o run --output-format csv -- \\
         python3 bench.py --workload W --steps 3 --warmup 1 --no-extra --no-cpu-baseline \\
-        --no-backward --no-varlen --no-splitkv --no-fp8    (W = 2..5, and WRITE_SIZE)
+        --no-backward --no-varlen --no-splitkv --no-fp8    (W = 1..5, and WRITE_SIZE)
     rocprofv3 --kernel-trace --pmc MfmaUtil SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE \\
         -d OUT/util_W -o run --output-format csv -- python3 bench.py --workload W \\
         --steps 20 --warmup 2 --no-extra --no-cpu-baseline --no-backward --no-varlen \\
-        --no-splitkv --no-fp8                              (W = 2..5)
+        --no-splitkv --no-fp8                              (W = 1..5)
 
 This is measurement tooling: it reads CSV files and imports bench.py for the
 workload definitions, algorithmic byte counts and the kernel source hash.
@@ -46,6 +46,18 @@ SES = 32       # 8 XCDs x 4 shader engines (SQ_BUSY_CYCLES is summed over them)
 XCDS = 8       # GRBM_GUI_ACTIVE is summed over the XCDs
 
 
+def csv_in(base, name):
+    """Path of rocprofv3's CSV `name` under the output directory `base` (directly in it, or in the
+    host/process subdirectories rocprofv3 may add)."""
+    direct = os.path.join(base, name)
+    if os.path.exists(direct):
+        return direct
+    for root, _, files in os.walk(base):
+        if name in files:
+            return os.path.join(root, name)
+    raise FileNotFoundError(f"{name} under {base}")
+
+
 def short_name(kernel_name):
     n = kernel_name.replace("void attn::(anonymous namespace)::", "").replace("(attn::Params)", "")
     n = n.replace("(attn::(anonymous namespace)::BwdParams)", "").replace("(attn::BwdParams)", "")
@@ -65,14 +77,20 @@ def dispatches(path, kernel_filter="attn_fwd_bf16_kernel"):
     return per, dur
 
 
+def forward_kernel(w):
+    """Name filter of the forward kernel that workload w launches."""
+    return "attn_fwd_f32_kernel" if WORKLOADS[w].dtype == "f32" else "attn_fwd_bf16_kernel"
+
+
 # --------------------------------------------------------------------------- trace
 
 TRACE_LABELS = {
-    ("attn_fwd_bf16_kernel<64, 4, false, 2, false, false>", 256): "forward, workload 2 (headline): mha B4 H8 N1024 d64",
+    ("attn_fwd_f32_kernel<64, false>", 2): "forward, workload 1 (fp32): single-head B1 H1 N256 d64",
+    ("attn_fwd_bf16_kernel<64, 4, false, 2, false, false>", 256): "forward, workload 2: mha B4 H8 N1024 d64",
     ("attn_fwd_bf16_kernel<64, 4, true, 2, true, false>", 256): "forward, workload 3: causal B2 H8 N4096 d64",
     ("attn_fwd_bf16_kernel<128, 8, true, 1, false, false>", 1024): "forward, workload 4: causal long B1 H16 N16384 d128",
     ("attn_fwd_bf16_kernel<128, 8, false, 1, false, false>", 2048):
-        "forward, workload 5: gqa padded B2 Hq32 Hkv8 N8192 d128",
+        "forward, workload 5 (headline): gqa padded B2 Hq32 Hkv8 N8192 d128",
     ("attn_fwd_bf16_kernel<128, 4, true, 1, false, true>", 16384):
         "packed varlen: 8 sequences U{4096..8192}, Hq32 Hkv8 d128 causal",
     ("attn_fwd_bf16_kernel<128, 4, true, 1, false, true>", 2048):
@@ -88,7 +106,7 @@ def trace(base, log):
     cmd = (f"rocprofv3 --kernel-trace --stats -d {base} -o run --output-format csv -- "
            "python3 bench.py --steps 50 --warmup 5 --no-cpu-baseline")
     groups = collections.OrderedDict()
-    for r in csv.DictReader(open(os.path.join(base, "run_kernel_trace.csv"))):
+    for r in csv.DictReader(open(csv_in(base, "run_kernel_trace.csv"))):
         wg = int(r["Workgroup_Size_X"])
         key = (short_name(r["Kernel_Name"]), int(r["Grid_Size_X"]) // wg, wg)
         groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
@@ -114,15 +132,16 @@ def trace(base, log):
                                for (lab, n, g, w, c, a, a2, m, mn, mx) in sel) + "\n"
 
     fwd = sorted([r for r in rows if r[0].startswith("forward")], key=lambda r: r[0])
-    md = f"""# rocprofv3 kernel-trace summary: attn_fwd_bf16_kernel, workloads 2 (headline) to 5
+    md = f"""# rocprofv3 kernel-trace summary: the forward kernels, workloads 1 to 5 (5 is the headline)
 
 Command (one MI355X, repository root), summarised by `python3 rocprof_summary.py trace`:
 
     {cmd}
 
-Template arguments are <D, WAVES, CAUSAL, KSPLIT, PERSISTENT, GENERAL> (WAVES: 32-row query
-slices per key-split group).  Durations in microseconds from run_kernel_trace.csv (the warm-up
-launches are included in the plain average, not in the second).
+Template arguments are attn_fwd_bf16_kernel <D, WAVES, CAUSAL, KSPLIT, PERSISTENT, GENERAL>
+(WAVES: 32-row query slices per key-split group) and attn_fwd_f32_kernel <D, CAUSAL>.
+Durations in microseconds from run_kernel_trace.csv (the warm-up launches are included in the
+plain average, not in the second).
 
 {table(fwd)}
 """
@@ -134,12 +153,12 @@ launches are included in the plain average, not in the second).
                f"the launch stream over {result['steps']} back-to-back launches; rocprofv3 gives {h[6]:.2f} us per "
                f"launch averaged over the calls after the first (median {h[7]:.2f} us), "
                f"{abs(ev - h[6]) / h[6] * 100:.1f}% apart (the events also count the gaps between launches).\n")
-    with open(os.path.join(PROFILES, "attn_fwd_bf16_workloads2-5_kernel_trace.md"), "w") as f:
+    with open(os.path.join(PROFILES, "attn_fwd_workloads1-5_kernel_trace.md"), "w") as f:
         f.write(md)
     other = [r for r in rows if not r[0].startswith("forward")]
     md2 = f"""# rocprofv3 kernel-trace summary: packed varlen, split-KV + merge, fp8 forward, backward
 
-Same run as attn_fwd_bf16_workloads2-5_kernel_trace.md:
+Same run as attn_fwd_workloads1-5_kernel_trace.md:
 
     {cmd}
 
@@ -164,8 +183,8 @@ def traffic(base):
         vals = [sum(v.values()) for _, v in sorted(per.items())]
         return statistics.median(vals)
 
-    f_copy = med(os.path.join(base, "tr_copy_FETCH_SIZE", "run_counter_collection.csv"), "copyBuffer")
-    w_copy = med(os.path.join(base, "tr_copy_WRITE_SIZE", "run_counter_collection.csv"), "copyBuffer")
+    f_copy = med(csv_in(os.path.join(base, "tr_copy_FETCH_SIZE"), "run_counter_collection.csv"), "copyBuffer")
+    w_copy = med(csv_in(os.path.join(base, "tr_copy_WRITE_SIZE"), "run_counter_collection.csv"), "copyBuffer")
     f_factor = copy_mib * 1024 / f_copy
     w_factor = copy_mib * 1024 / w_copy
     out = {"kernel_source_hash": bench.kernel_source_hash(),
@@ -173,9 +192,9 @@ def traffic(base):
                            "fetch_factor": round(f_factor, 4), "write_factor": round(w_factor, 4)},
            "workloads": {}}
     lines = []
-    for w in (2, 3, 4, 5):
-        fk = med(os.path.join(base, f"tr_FETCH_SIZE_{w}", "run_counter_collection.csv"), "attn_fwd_bf16_kernel")
-        wk = med(os.path.join(base, f"tr_WRITE_SIZE_{w}", "run_counter_collection.csv"), "attn_fwd_bf16_kernel")
+    for w in (1, 2, 3, 4, 5):
+        fk = med(csv_in(os.path.join(base, f"tr_FETCH_SIZE_{w}"), "run_counter_collection.csv"), forward_kernel(w))
+        wk = med(csv_in(os.path.join(base, f"tr_WRITE_SIZE_{w}"), "run_counter_collection.csv"), forward_kernel(w))
         b = fk * 1024 * f_factor + wk * 1024 * w_factor
         alg = bench.algorithmic_bytes(WORKLOADS[w])
         out["workloads"][str(w)] = {"fetch_kib": fk, "write_kib": wk, "bytes_per_launch": int(b),
@@ -184,7 +203,7 @@ def traffic(base):
                      f"| {b / alg:.2f} |")
     with open(os.path.join(PROFILES, "hbm_traffic.json"), "w") as f:
         json.dump(out, f, indent=1)
-    md = f"""# HBM traffic of attn_fwd_bf16_kernel per launch (rocprofv3 counters)
+    md = f"""# HBM traffic of the forward kernel per launch, workloads 1 to 5 (rocprofv3 counters)
 
 Commands (one MI355X, repository root; one counter per pass), summarised by
 `python3 rocprof_summary.py traffic {base}`:
@@ -204,7 +223,7 @@ Kernel source hash (bench.kernel_source_hash): `{out['kernel_source_hash']}`.
 | workload | name | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled MiB | algorithmic MiB | ratio |
 |---|---|---|---|---|---|---|
 """ + "\n".join(lines) + "\n"
-    with open(os.path.join(PROFILES, "attn_fwd_bf16_hbm_traffic.md"), "w") as f:
+    with open(os.path.join(PROFILES, "attn_fwd_workloads1-5_hbm_traffic.md"), "w") as f:
         f.write(md)
     print(md)
 
@@ -214,8 +233,8 @@ Kernel source hash (bench.kernel_source_hash): `{out['kernel_source_hash']}`.
 def util(base):
     out = {"kernel_source_hash": bench.kernel_source_hash(), "workloads": {}}
     lines = []
-    for w in (2, 3, 4, 5):
-        per, dur = dispatches(os.path.join(base, f"util_{w}", "run_counter_collection.csv"))
+    for w in (1, 2, 3, 4, 5):
+        per, dur = dispatches(csv_in(os.path.join(base, f"util_{w}"), "run_counter_collection.csv"), forward_kernel(w))
         recs = []
         for d, c in sorted(per.items()):
             ns = dur[d]
@@ -231,14 +250,15 @@ def util(base):
                      f"{100 * med['mfma_busy']:.1f}% | {100 * med['rocprof_MfmaUtil']:.1f}% |")
     with open(os.path.join(PROFILES, "mfma_util.json"), "w") as f:
         json.dump(out, f, indent=1)
-    md = f"""# MFMA utilisation and shader clock of attn_fwd_bf16_kernel (rocprofv3 counters)
+    md = f"""# MFMA utilisation and shader clock of the forward kernel, workloads 1 to 5 (rocprofv3 counters)
 
 Command per workload W (one MI355X, repository root), summarised by
 `python3 rocprof_summary.py util {base}`:
 
     rocprofv3 --kernel-trace --pmc MfmaUtil SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE -d {base}/util_W -o run --output-format csv -- python3 bench.py --workload W --steps 20 --warmup 2 {BENCH_FLAGS}
 
-Per launch: `SQ_VALU_MFMA_BUSY_CYCLES` (summed over the 1024 SIMDs; 32 per 32x32x16 bf16 MFMA)
+Per launch: `SQ_VALU_MFMA_BUSY_CYCLES` (summed over the 1024 SIMDs; 32 per 32x32x16 bf16 MFMA,
+64 per 32x32x2 fp32 MFMA of workload 1)
 / 1024 is the matrix-core busy time of one SIMD; `SQ_BUSY_CYCLES` (summed over the 32 shader
 engines) / 32 is the number of shader-clock cycles with waves present, and divided by the
 launch's duration it gives the effective shader clock.  "MFMA busy" is the ratio of the two;
@@ -246,14 +266,18 @@ launch's duration it gives the effective shader clock.  "MFMA busy" is the ratio
 short launches also count time outside the kernel).  Medians over the launches after the first.
 
 The bf16 peak of 2.5 PFLOP/s assumes a 2.4 GHz clock: achieved TFLOP/s ≈ 2500 × (clock / 2.4)
-× MFMA busy × (algorithmic / executed MFMA flops).
+× MFMA busy × (algorithmic / executed MFMA flops) (workload 1: 157.3 in place of 2500).
+
+Workload 1 launches two workgroups: the shader engines without waves count no busy cycles, so
+its "clock" (cycles with waves present, averaged over all 32 engines) and "MFMA busy" are not
+utilisation figures of the chip; it is launch-latency bound.
 
 Kernel source hash (bench.kernel_source_hash): `{out['kernel_source_hash']}`.
 
 | workload | name | launches | us | shader clock GHz | MFMA busy | rocprof MfmaUtil |
 |---|---|---|---|---|---|---|
 """ + "\n".join(lines) + "\n"
-    with open(os.path.join(PROFILES, "attn_fwd_bf16_mfma_util.md"), "w") as f:
+    with open(os.path.join(PROFILES, "attn_fwd_workloads1-5_mfma_util.md"), "w") as f:
         f.write(md)
     print(md)
 
