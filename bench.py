@@ -235,6 +235,54 @@ class Fp8Runner(Runner):
                      None if self.kl is None else self.kl.data_ptr(), self.stream.cuda_stream)
 
 
+class Fp8PrepRunner(Runner):
+    """The fp8 preparation of a workload's bf16 q, k, v on the GPU, as one
+    step: amax and rotated quantisation of q and of k (one random-sign
+    Hadamard rotation for both), amax and transposed quantisation of V (six
+    C-ABI calls, nine kernels, no host synchronisation in between)."""
+
+    def __init__(self, w, dev):
+        import torch
+
+        import exact_tiled_attention_14_amd as attn
+        from workloads import make_inputs
+
+        self.w = w
+        q, k, v, _ = make_inputs(w)
+        self.q, self.k, self.v = q.to(dev), k.to(dev), v.to(dev)
+        self.signs = attn.hadamard_signs(w.d, seed=w.seed, device=dev)
+        self.q8 = torch.empty(self.q.shape, dtype=torch.float8_e4m3fn, device=dev)
+        self.k8 = torch.empty(self.k.shape, dtype=torch.float8_e4m3fn, device=dev)
+        self.n16 = (w.N + 15) // 16 * 16
+        self.vt8 = torch.empty((w.B, w.Hkv, w.d, self.n16), dtype=torch.float8_e4m3fn, device=dev)
+        self.scal = torch.zeros(3 * 8, dtype=torch.float32, device=dev)
+        self.stream = torch.cuda.current_stream(dev)
+        self.attn = attn
+
+    def launch(self):
+        a, w, st, sp = self.attn, self.w, self.stream.cuda_stream, self.signs.data_ptr()
+        rq, rk = w.B * w.H * w.N, w.B * w.Hkv * w.N
+        sc = [self.scal[8 * i:].data_ptr() for i in range(3)]
+        ds = [self.scal[8 * i + 4:].data_ptr() for i in range(3)]
+        codes = (a.attn_fp8_amax(self.q.data_ptr(), sp, rq, w.d, sc[0], st),
+                 a.attn_fp8_quantize(self.q.data_ptr(), sp, rq, w.d, sc[0], self.q8.data_ptr(), ds[0], st),
+                 a.attn_fp8_amax(self.k.data_ptr(), sp, rk, w.d, sc[1], st),
+                 a.attn_fp8_quantize(self.k.data_ptr(), sp, rk, w.d, sc[1], self.k8.data_ptr(), ds[1], st),
+                 a.attn_fp8_amax(self.v.data_ptr(), None, rk, w.d, sc[2], st),
+                 a.attn_fp8_quantize_vt(self.v.data_ptr(), w.B * w.Hkv, w.N, w.d, sc[2], self.vt8.data_ptr(), ds[2],
+                                        st))
+        if any(c != 0 for c in codes):
+            raise RuntimeError(f"fp8 preparation failed with status {codes}")
+
+    def bytes(self):
+        """(compulsory bytes: every bf16 input read once and every fp8 byte
+        written once; bytes of the two passes: the inputs read twice)."""
+        w = self.w
+        n_in = (w.B * w.H + 2 * w.B * w.Hkv) * w.N * w.d
+        n_out = (w.B * w.H + w.B * w.Hkv) * w.N * w.d + w.B * w.Hkv * w.d * self.n16
+        return 2 * n_in + n_out, 4 * n_in + n_out
+
+
 class VarlenRunner(Runner):
     """The packed variable-length batch (attn_fwd_varlen_bf16) resident on the GPU."""
 
@@ -551,6 +599,19 @@ def main():
                              "steps_per_region": st, "algorithmic_tflops": round(rate(a, m), 2),
                              "frac_of_fp8_peak": round(rate(a, m) / PEAK_FP8_TFLOPS, 4)}
             del fr
+            # the preparation (incoherent-processing rotation and quantisation) of the
+            # same shape's bf16 inputs: HBM-bound, against 8 TB/s
+            pr = Fp8PrepRunner(ww, dev)
+            m, st, _ = pr.time(max(10, min(args.steps, 50)), 3, args.repeats, min_region_ms=MIN_REGION_MS)
+            compulsory, passes = pr.bytes()
+            fp8[str(wid)]["prep"] = {
+                "what": ("rotate + amax + quantise q and k, amax + transposed quantise of v "
+                         "(6 C-ABI calls, 9 kernels)"),
+                "ms": round(m, 4), "steps_per_region": st,
+                "compulsory_bytes": compulsory, "compulsory_gbs": round(compulsory / (m * 1e-3) / 1e9, 1),
+                "two_pass_bytes": passes, "two_pass_gbs": round(passes / (m * 1e-3) / 1e9, 1),
+                "frac_of_hbm_peak": round(passes / (m * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+            del pr
         line["fp8"] = fp8
 
     if not args.no_splitkv:

@@ -26,7 +26,10 @@ namespace {
 
 constexpr float kE4m3Max = 448.0f;
 
-// The 8 values a lane holds, rotated: y = H_D · (s ∘ x) (not yet divided by √D).
+// The 8 values a lane holds, rotated: y = H_D · x (the signs already applied,
+// not yet divided by √D).  A cross-lane round takes the partner's value p and
+// keeps x + p in the lane whose bit m is clear, p − x in the other: both are
+// fma(±1, x, p), exactly.
 template <int D>
 __device__ __forceinline__ void fwht(float (&x)[8], int l) {
 #pragma unroll
@@ -40,12 +43,11 @@ __device__ __forceinline__ void fwht(float (&x)[8], int l) {
             }
     constexpr int LPR = D / 8;  // lanes per row
 #pragma unroll
-    for (int m = 1; m < LPR; m <<= 1)
+    for (int m = 1; m < LPR; m <<= 1) {
+        const float sg = (l & m) ? -1.0f : 1.0f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float p = __shfl_xor(x[e], m, 64);
-            x[e] = (l & m) ? (p - x[e]) : (x[e] + p);
-        }
+        for (int e = 0; e < 8; ++e) x[e] = __builtin_fmaf(sg, x[e], __shfl_xor(x[e], m, 64));
+    }
 }
 
 // 1/√D in fp32
@@ -63,19 +65,27 @@ __device__ __forceinline__ void unpack_bf16x8(const uint4& u, float (&x)[8]) {
     }
 }
 
-// Row r's 8 values of this lane, rotated (when signs is not NULL: R x, with
-// the division by √D); zeros for a row past the end.
-template <int D>
-__device__ __forceinline__ void load_rotated(const uint16_t* x, const float* signs, int64_t rows, int64_t r, int l,
-                                             float (&v)[8]) {
-    uint4 u = make_uint4(0u, 0u, 0u, 0u);
-    if (r < rows) u = *reinterpret_cast<const uint4*>(x + r * D + 8 * l);
-    unpack_bf16x8(u, v);
+// This lane's 8 signs (all 1 when signs is NULL: no rotation).
+__device__ __forceinline__ void load_signs(const float* signs, int l, float (&sg)[8]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sg[e] = 1.0f;
     if (signs != nullptr) {
         const float4 s0 = *reinterpret_cast<const float4*>(signs + 8 * l);
         const float4 s1 = *reinterpret_cast<const float4*>(signs + 8 * l + 4);
-        v[0] *= s0.x; v[1] *= s0.y; v[2] *= s0.z; v[3] *= s0.w;
-        v[4] *= s1.x; v[5] *= s1.y; v[6] *= s1.z; v[7] *= s1.w;
+        sg[0] = s0.x; sg[1] = s0.y; sg[2] = s0.z; sg[3] = s0.w;
+        sg[4] = s1.x; sg[5] = s1.y; sg[6] = s1.z; sg[7] = s1.w;
+    }
+}
+
+// A lane's 16 bytes (8 values) of row r as floats, rotated when ROT (R x:
+// signs, transform, division by √D); the caller passes zeros for rows past
+// the end.
+template <int D, bool ROT>
+__device__ __forceinline__ void rotated(const uint4& u, const float (&sg)[8], int l, float (&v)[8]) {
+    unpack_bf16x8(u, v);
+    if (ROT) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] *= sg[e];
         fwht<D>(v, l);
         const float f = inv_sqrt_d<D>();
 #pragma unroll
@@ -85,21 +95,40 @@ __device__ __forceinline__ void load_rotated(const uint16_t* x, const float* sig
 
 __global__ void zero_kernel(float* p) { *p = 0.0f; }
 
+// Steps of RPW rows that one wave loads before it uses any (loads in flight
+// per lane).
+constexpr int kUnroll = 4;
+
 // amax = max |R x| over every element (|x| when signs is NULL; NaN entries
 // take no part).  Non-negative floats order like their bit patterns, so the
-// workgroups combine their maxima with an integer atomic max.
-template <int D>
+// workgroups combine their maxima with an integer atomic max, issued only by
+// a workgroup whose maximum exceeds the value already there.
+template <int D, bool ROT>
 __global__ __launch_bounds__(256) void amax_kernel(const uint16_t* x, const float* signs, int64_t rows, float* amax) {
-    constexpr int LPR = D / 8, RPW = 64 / LPR;
+    constexpr int LPR = D / 8, RPW = 64 / LPR, U = kUnroll;
     const int lane = threadIdx.x & 63, l = lane % LPR;
     const int64_t waves = (int64_t)gridDim.x * (blockDim.x >> 6);
     const int64_t w = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    float sg[8];
+    load_signs(ROT ? signs : nullptr, l, sg);
     float m = 0.0f;
-    for (int64_t r0 = w * RPW; r0 < rows; r0 += waves * RPW) {
-        float v[8];
-        load_rotated<D>(x, signs, rows, r0 + lane / LPR, l, v);
+    // (the loop runs on the wave's first row, the same for all its lanes: the
+    // transform's lane exchanges need every lane; rows past the end are zeros)
+    for (int64_t rb = w * RPW * U; rb < rows; rb += waves * RPW * U) {
+        const int64_t r0 = rb + lane / LPR;
+        uint4 u[U];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[e]));  // (fmaxf skips a NaN operand)
+        for (int k = 0; k < U; ++k) {
+            const int64_t r = r0 + k * RPW;
+            u[k] = r < rows ? *reinterpret_cast<const uint4*>(x + r * D + 8 * l) : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            float v[8];
+            rotated<D, ROT>(u[k], sg, l, v);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[e]));  // (fmaxf skips a NaN operand)
+        }
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
@@ -109,7 +138,8 @@ __global__ __launch_bounds__(256) void amax_kernel(const uint16_t* x, const floa
     if (threadIdx.x == 0) {
         float t = part[0];
         for (int i = 1; i < (int)(blockDim.x >> 6); ++i) t = fmaxf(t, part[i]);
-        atomicMax(reinterpret_cast<unsigned int*>(amax), __float_as_uint(t));
+        unsigned int* a = reinterpret_cast<unsigned int*>(amax);
+        if (__float_as_uint(t) > __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(a, __float_as_uint(t));
     }
 }
 
@@ -129,30 +159,55 @@ __device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float 
 
 // x8[r][:] = e4m3(R x[r] / descale), descale from the device amax; block 0
 // also writes descale out.
-template <int D>
+template <int D, bool ROT>
 __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* x, const float* signs, int64_t rows,
                                                        const float* amax, uint8_t* x8, float* descale_out) {
-    constexpr int LPR = D / 8, RPW = 64 / LPR;
+    constexpr int LPR = D / 8, RPW = 64 / LPR, U = kUnroll;
     const int lane = threadIdx.x & 63, l = lane % LPR;
     const float ds = descale_of(*amax);
     const float inv = 1.0f / ds;
     if (blockIdx.x == 0 && threadIdx.x == 0) *descale_out = ds;
     const int64_t waves = (int64_t)gridDim.x * (blockDim.x >> 6);
     const int64_t w = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-    for (int64_t r0 = w * RPW; r0 < rows; r0 += waves * RPW) {
-        const int64_t r = r0 + lane / LPR;
-        float v[8];
-        load_rotated<D>(x, signs, rows, r, l, v);
-        const uint32_t lo = pack4_e4m3(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
-        const uint32_t hi = pack4_e4m3(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
-        if (r < rows) *reinterpret_cast<uint2*>(x8 + r * D + 8 * l) = make_uint2(lo, hi);
+    float sg[8];
+    load_signs(ROT ? signs : nullptr, l, sg);
+    // (the loop runs on the wave's first row, the same for all its lanes: the
+    // transform's lane exchanges need every lane; rows past the end are zeros)
+    for (int64_t rb = w * RPW * U; rb < rows; rb += waves * RPW * U) {
+        const int64_t r0 = rb + lane / LPR;
+        uint4 u[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int64_t r = r0 + k * RPW;
+            u[k] = r < rows ? *reinterpret_cast<const uint4*>(x + r * D + 8 * l) : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int64_t r = r0 + k * RPW;
+            float v[8];
+            rotated<D, ROT>(u[k], sg, l, v);
+            const uint32_t lo = pack4_e4m3(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+            const uint32_t hi = pack4_e4m3(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
+            if (r < rows) *reinterpret_cast<uint2*>(x8 + r * D + 8 * l) = make_uint2(lo, hi);
+        }
     }
+}
+
+// Byte e (0..3) of each of a, b, c, d, in that order, in one word.
+__device__ __forceinline__ uint32_t gather_byte(uint32_t a, uint32_t b, uint32_t c, uint32_t d, int e) {
+    // v_perm_b32: selector byte i picks byte sel_i of the pair (hi word, lo word)
+    // = bytes 7..4 of the first operand, 3..0 of the second; 0x0c gives 0
+    const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0c0c0000u | ((4u + e) << 8) | (uint32_t)e);
+    const uint32_t cd = __builtin_amdgcn_perm(d, c, ((4u + e) << 24) | ((uint32_t)e << 16) | 0x0c0cu);
+    return ab | cd;
 }
 
 // V [heads][N][D] bf16 -> Vᵀ [heads][D][ldvt] e4m3 (ldvt = N rounded up to a
 // multiple of 16; columns N .. ldvt − 1 are written as 0).  One workgroup per
-// (head, 64 keys): the 64 × D tile is read with 16-byte loads, converted, and
-// written transposed into LDS, then stored as D rows of 64 bytes.
+// (head, 64 keys): a thread converts 4 consecutive keys at 8 consecutive d
+// (four 16-byte loads), gathers the 4 key bytes of each d into one word and
+// writes it transposed into LDS; then the tile is stored as D rows of 64
+// bytes.
 template <int D>
 __global__ __launch_bounds__(256) void quantize_vt_kernel(const uint16_t* v, int N, int ldvt, const float* amax,
                                                           uint8_t* vt8, float* descale_out) {
@@ -165,19 +220,28 @@ __global__ __launch_bounds__(256) void quantize_vt_kernel(const uint16_t* v, int
     const float inv = 1.0f / ds;
     if (blockIdx.x == 0 && threadIdx.x == 0) *descale_out = ds;
     const uint16_t* src = v + head * (int64_t)N * D;
-    // 64 keys x D values = 8·D 16-byte pieces
-    for (int i = threadIdx.x; i < 8 * D; i += blockDim.x) {
-        const int key = i / (D / 8), c0 = (i % (D / 8)) * 8;
-        uint4 u = make_uint4(0u, 0u, 0u, 0u);
-        if (k0 + key < N) u = *reinterpret_cast<const uint4*>(src + (int64_t)(k0 + key) * D + c0);
-        float x[8];
-        unpack_bf16x8(u, x);
-        const uint32_t lo = pack4_e4m3(x[0] * inv, x[1] * inv, x[2] * inv, x[3] * inv);
-        const uint32_t hi = pack4_e4m3(x[4] * inv, x[5] * inv, x[6] * inv, x[7] * inv);
+    // 16 groups of 4 keys x D / 8 groups of 8 d
+    for (int t = threadIdx.x; t < 16 * (D / 8); t += blockDim.x) {
+        const int kg = t % 16, c0 = (t / 16) * 8;
+        uint4 u[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int key = k0 + 4 * kg + j;
+            u[j] = key < N ? *reinterpret_cast<const uint4*>(src + (int64_t)key * D + c0) : make_uint4(0u, 0u, 0u, 0u);
+        }
+        uint32_t lo[4], hi[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float x[8];
+            unpack_bf16x8(u[j], x);
+            lo[j] = pack4_e4m3(x[0] * inv, x[1] * inv, x[2] * inv, x[3] * inv);
+            hi[j] = pack4_e4m3(x[4] * inv, x[5] * inv, x[6] * inv, x[7] * inv);
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            tile[(c0 + e) * PITCH + key] = (uint8_t)(lo >> (8 * e));
-            tile[(c0 + 4 + e) * PITCH + key] = (uint8_t)(hi >> (8 * e));
+            *reinterpret_cast<uint32_t*>(tile + (c0 + e) * PITCH + 4 * kg) = gather_byte(lo[0], lo[1], lo[2], lo[3], e);
+            *reinterpret_cast<uint32_t*>(tile + (c0 + 4 + e) * PITCH + 4 * kg) =
+                gather_byte(hi[0], hi[1], hi[2], hi[3], e);
         }
     }
     __syncthreads();
@@ -191,33 +255,42 @@ __global__ __launch_bounds__(256) void quantize_vt_kernel(const uint16_t* v, int
     }
 }
 
-int grid_for(int64_t rows, int d) {
-    const int64_t per_block = 4 * (64 / (d / 8));  // rows per workgroup step
+// Workgroups of a grid-stride launch over `rows` rows: enough for every row
+// step once, at most `cap`.
+int grid_for(int64_t rows, int d, int cap) {
+    const int64_t per_block = 4 * kUnroll * (64 / (d / 8));  // rows per workgroup iteration
     const int64_t g = (rows + per_block - 1) / per_block;
-    return (int)(g < 4096 ? (g < 1 ? 1 : g) : 4096);
+    return (int)(g < cap ? (g < 1 ? 1 : g) : cap);
 }
 
 }  // namespace
 
 hipError_t launch_fp8_amax(const void* x, const float* signs, int64_t rows, int d, float* amax, hipStream_t stream) {
     hipLaunchKernelGGL(zero_kernel, dim3(1), dim3(1), 0, stream, amax);
-    const dim3 grid((unsigned)grid_for(rows, d)), block(256);
-    if (d == 64)
-        hipLaunchKernelGGL(amax_kernel<64>, grid, block, 0, stream, static_cast<const uint16_t*>(x), signs, rows, amax);
-    else
-        hipLaunchKernelGGL(amax_kernel<128>, grid, block, 0, stream, static_cast<const uint16_t*>(x), signs, rows, amax);
+    const dim3 grid((unsigned)grid_for(rows, d, 1024)), block(256);
+    const uint16_t* xp = static_cast<const uint16_t*>(x);
+    if (d == 64) {
+        if (signs) hipLaunchKernelGGL((amax_kernel<64, true>), grid, block, 0, stream, xp, signs, rows, amax);
+        else hipLaunchKernelGGL((amax_kernel<64, false>), grid, block, 0, stream, xp, signs, rows, amax);
+    } else {
+        if (signs) hipLaunchKernelGGL((amax_kernel<128, true>), grid, block, 0, stream, xp, signs, rows, amax);
+        else hipLaunchKernelGGL((amax_kernel<128, false>), grid, block, 0, stream, xp, signs, rows, amax);
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_fp8_quantize(const void* x, const float* signs, int64_t rows, int d, const float* amax, void* x8,
                                float* descale, hipStream_t stream) {
-    const dim3 grid((unsigned)grid_for(rows, d)), block(256);
-    if (d == 64)
-        hipLaunchKernelGGL(quantize_kernel<64>, grid, block, 0, stream, static_cast<const uint16_t*>(x), signs, rows,
-                           amax, static_cast<uint8_t*>(x8), descale);
-    else
-        hipLaunchKernelGGL(quantize_kernel<128>, grid, block, 0, stream, static_cast<const uint16_t*>(x), signs, rows,
-                           amax, static_cast<uint8_t*>(x8), descale);
+    const dim3 grid((unsigned)grid_for(rows, d, 4096)), block(256);
+    const uint16_t* xp = static_cast<const uint16_t*>(x);
+    uint8_t* o = static_cast<uint8_t*>(x8);
+    if (d == 64) {
+        if (signs) hipLaunchKernelGGL((quantize_kernel<64, true>), grid, block, 0, stream, xp, signs, rows, amax, o, descale);
+        else hipLaunchKernelGGL((quantize_kernel<64, false>), grid, block, 0, stream, xp, signs, rows, amax, o, descale);
+    } else {
+        if (signs) hipLaunchKernelGGL((quantize_kernel<128, true>), grid, block, 0, stream, xp, signs, rows, amax, o, descale);
+        else hipLaunchKernelGGL((quantize_kernel<128, false>), grid, block, 0, stream, xp, signs, rows, amax, o, descale);
+    }
     return hipGetLastError();
 }
 
