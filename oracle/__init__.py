@@ -15,7 +15,11 @@ finite differences and invariants in ``tests/test_oracle_backward.py``; the
 packed-sequence form against brute force and invariants in
 ``tests/test_oracle_varlen.py``; the key-block partials and the S-way merge
 against brute force, the full definition and invariants in
-``tests/test_oracle_partial.py``.  No
+``tests/test_oracle_partial.py``; the fp8 pieces (``oracle/fp8.py``: e4m3
+rounding, per-tensor quantisation, the Hadamard rotation of incoherent
+processing) against the e4m3 bit layout decoded by hand, torch's e4m3 cast,
+closed forms of the Hadamard matrix and the invariance of attention under the
+rotation, with planted mistakes, in ``tests/test_oracle_fp8.py``.  No
 function here is "parity unpinned".
 """
 
