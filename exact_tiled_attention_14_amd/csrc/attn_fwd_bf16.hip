@@ -26,8 +26,9 @@
 // epilogue checks ℓ and Oᵀ, and if any row of the workgroup is not finite the
 // whole workgroup recomputes its rows with the exact running-max update
 // (safe_softmax_block: α = 2^(m_old − m_new) rescales ℓ and Oᵀ) on every
-// 32-key block, which cannot overflow.  ℓ sums the fp32 P (summing the bf16-rounded P would move LSE by
-// up to 2^-9 on short rows).
+// 32-key block, which cannot overflow.  ℓ sums the fp32 P (summing the
+// bf16-rounded P would move LSE by up to ln(1 + 2^-8) on short rows: bf16
+// keeps 8 significant bits).
 //
 // Register layouts.  The MFMA computes Sᵀ (keys × queries) so that a lane owns
 // ONE query row (lane % 32) and 16 keys of every 32-key block, so row sums are

@@ -2,12 +2,13 @@
 the fp64 backward oracle, on bf16 inputs.
 
 Tolerance: max |grad_gpu − grad_oracle| ≤ 2e-2 · max |grad_oracle| per tensor
-(dQ, dK, dV).  The gradients are stored in bf16 (relative rounding 2^-9), and
+(dQ, dK, dV).  The gradients are stored in bf16 (relative rounding up to
+2^-8: 8 significant bits, nearest), and
 inside the kernels P and dS are rounded to bf16 as matrix-core operands and D
 is formed from the bf16 forward output; each of these is a relative
-perturbation of order 2^-9 of terms that are summed over up to N keys or
-queries with mixed signs, so the bound leaves a margin of about 10× over
-2^-9 on the largest gradient entry.  No NaN may appear.
+perturbation of order 2^-8 of terms that are summed over up to N keys or
+queries with mixed signs, so the bound leaves a margin of about 5× over
+2^-8 on the largest gradient entry.  No NaN may appear.
 """
 
 import math
@@ -204,7 +205,8 @@ def _column_sums(wid, w, inputs, grads):
     admissible row's weights sum to one, so for every kv head the dV rows
     summed over the keys equal the dO rows summed over that head's query
     heads; padded keys get exactly zero gradients.  Tolerance: the weights
-    are bf16 operands (2^-9 each) and dV is stored in bf16."""
+    are bf16 operands (relative rounding up to 2^-8 each) and dV is stored in
+    bf16."""
     q, k, v, do, kl = inputs
     dq, dk, dv = grads
     group = w.H // w.Hkv

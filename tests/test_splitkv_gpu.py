@@ -4,7 +4,7 @@ oracle: the key-block partial (attn_fwd_partial_bf16), the S-way merge
 
 Tolerances: O of a bf16-input attention ≤ 1.5e-2 and LSE ≤ 1e-3 (as for the
 dense path; the split-KV forward keeps its partial O in bf16, which adds one
-rounding of 2^-9 relative before the merge, far inside that bound, and its
+rounding of up to 2^-8 relative before the merge, far inside that bound, and its
 partial LSE in fp32);
 the merge of given fp32 partials ≤ 1e-5 (fp32 output) or half a bf16 unit of
 the output magnitude (bf16 output), LSE ≤ 1e-5.
