@@ -12,7 +12,7 @@
 
 namespace attn {
 hipError_t launch_fwd_bf16(const Params& p, int d, bool causal, const Schedule& sc, hipStream_t stream);
-hipError_t launch_fwd_f32(const Params& p, int d, bool causal, hipStream_t stream);
+hipError_t launch_fwd_f32(const Params& p, int d, bool causal, bool small, hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdParams& p, int d, bool causal, hipStream_t stream);
 hipError_t launch_fwd_fp8(const Params& p, int d, bool causal, hipStream_t stream);
 hipError_t launch_merge(const float* o_parts, const float* lse_parts, int S, int64_t rows, int d, void* o,
@@ -149,7 +149,8 @@ int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float
     const int st = validate(q, k, v, o, lse, B, H, Hkv, N, d, scale, causal, key_lens, &p, &empty);
     if (st != ATTN_OK || empty) return st;
     (void)hipGetLastError();
-    const hipError_t e = attn::launch_fwd_f32(p, d, causal != 0, static_cast<hipStream_t>(stream));
+    const bool small = (int64_t)p.B * p.H * p.q_tiles < device_cus();
+    const hipError_t e = attn::launch_fwd_f32(p, d, causal != 0, small, static_cast<hipStream_t>(stream));
     return hip_status(e);
 }
 
