@@ -11,14 +11,17 @@
 // both q and k it keeps every score q·k, and it spreads an outlier channel
 // over all d channels before the per-tensor scale is chosen.
 //
-// Layout: a row of d = 64 or 128 bf16 values is held by d / 8 consecutive
-// lanes, 8 values (16 bytes) each, so one wave covers 64 / (d / 8) rows per
-// step with coalesced 16-byte loads.  Element e of lane l (within the row) is
-// index 8l + e.  H_d · z is the fast Walsh–Hadamard transform: for every bit
-// b of the index, the pairs (i, i + 2^b) with bit b clear become (z_i +
-// z_{i+2^b}, z_i − z_{i+2^b}); bits 0..2 are inside a lane, the higher bits
-// between lanes (a lane exchange with lane ^ 2^(b−3)).  These kernels are
-// bound by HBM (2 bytes read and 1 written per element).
+// Layout: a row of d = 64 or 128 bf16 values is held by d / 8 lanes, 8 values
+// (16 bytes) each, so one wave covers 64 / (d / 8) consecutive rows per step
+// (1 KiB, one coalesced load instruction).  Element e of the lane at position
+// g of its row is index 8g + e.  The bits of g sit on lane bits 0, 1, 4 and 5
+// (d = 128; 0, 1, 4 for d = 64) and the row on the other lane bits, so that
+// every exchange between the lanes of a row is a DPP quad permutation (lane
+// bits 0, 1) or a v_permlane16/32_swap (lane bits 4, 5), no LDS round trip.
+// H_d · z is the fast Walsh–Hadamard transform: for every bit b of the index,
+// the pairs (i, i + 2^b) with bit b clear become (z_i + z_{i+2^b},
+// z_i − z_{i+2^b}); bits 0..2 are inside a lane, the higher bits between
+// lanes.  The data is 2 bytes read and 1 written per element.
 #include "attn_common.h"
 
 namespace attn {
@@ -26,12 +29,41 @@ namespace {
 
 constexpr float kE4m3Max = 448.0f;
 
-// The 8 values a lane holds, rotated: y = H_D · x (the signs already applied,
-// not yet divided by √D).  A cross-lane round takes the partner's value p and
-// keeps x + p in the lane whose bit m is clear, p − x in the other: both are
-// fma(±1, x, p), exactly.
+// Position of a lane within its row (g, d / 8 of them) and the row of the
+// wave step it loads (rr).
 template <int D>
-__device__ __forceinline__ void fwht(float (&x)[8], int l) {
+__device__ __forceinline__ int row_pos(int lane) {
+    return D == 128 ? ((lane & 3) | ((lane >> 2) & 12)) : ((lane & 3) | ((lane >> 2) & 4));
+}
+template <int D>
+__device__ __forceinline__ int row_of(int lane) {
+    return D == 128 ? ((lane >> 2) & 3) : (((lane >> 2) & 3) | ((lane >> 3) & 4));
+}
+
+// One butterfly between lanes: the lane whose exchanged bit is clear keeps
+// x + p, the other p − x (p the partner's value), both exactly fma(±1, x, p).
+template <int CTRL>
+__device__ __forceinline__ float xchg_dpp(float x, float sg) {
+    const float p = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+    return __builtin_fmaf(sg, x, p);
+}
+// v_permlane16_swap / v_permlane32_swap of x with itself: the first result is
+// x of the lane whose bit is clear, the second that of the lane whose bit is
+// set (each lane gets its own value in one, its partner's in the other), so
+// the butterfly is first + sign · second.
+__device__ __forceinline__ float xchg16(float x, float sg) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __builtin_fmaf(sg, __uint_as_float(r[1]), __uint_as_float(r[0]));
+}
+__device__ __forceinline__ float xchg32(float x, float sg) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __builtin_fmaf(sg, __uint_as_float(r[1]), __uint_as_float(r[0]));
+}
+
+// The 8 values a lane holds, rotated: y = H_D · x (the signs already applied,
+// not yet divided by √D).
+template <int D>
+__device__ __forceinline__ void fwht(float (&x)[8], int lane) {
 #pragma unroll
     for (int b = 1; b < 8; b <<= 1)
 #pragma unroll
@@ -41,12 +73,18 @@ __device__ __forceinline__ void fwht(float (&x)[8], int l) {
                 x[e] = a + c;
                 x[e | b] = a - c;
             }
-    constexpr int LPR = D / 8;  // lanes per row
+    // index bits 3, 4, 5 (, 6): lane bits 0, 1, 4 (, 5)
+    const float s0 = (lane & 1) ? -1.0f : 1.0f, s1 = (lane & 2) ? -1.0f : 1.0f;
+    const float s4 = (lane & 16) ? -1.0f : 1.0f, s5 = (lane & 32) ? -1.0f : 1.0f;
 #pragma unroll
-    for (int m = 1; m < LPR; m <<= 1) {
-        const float sg = (l & m) ? -1.0f : 1.0f;
+    for (int e = 0; e < 8; ++e) x[e] = xchg_dpp<0xB1>(x[e], s0);  // quad_perm [1, 0, 3, 2]: lane ^ 1
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = __builtin_fmaf(sg, x[e], __shfl_xor(x[e], m, 64));
+    for (int e = 0; e < 8; ++e) x[e] = xchg_dpp<0x4E>(x[e], s1);  // quad_perm [2, 3, 0, 1]: lane ^ 2
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = xchg16(x[e], s4);
+    if (D == 128) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = xchg32(x[e], s5);
     }
 }
 
@@ -65,7 +103,8 @@ __device__ __forceinline__ void unpack_bf16x8(const uint4& u, float (&x)[8]) {
     }
 }
 
-// This lane's 8 signs (all 1 when signs is NULL: no rotation).
+// The 8 signs of this lane's row position l (all 1 when signs is NULL: no
+// rotation).
 __device__ __forceinline__ void load_signs(const float* signs, int l, float (&sg)[8]) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) sg[e] = 1.0f;
@@ -81,12 +120,12 @@ __device__ __forceinline__ void load_signs(const float* signs, int l, float (&sg
 // signs, transform, division by √D); the caller passes zeros for rows past
 // the end.
 template <int D, bool ROT>
-__device__ __forceinline__ void rotated(const uint4& u, const float (&sg)[8], int l, float (&v)[8]) {
+__device__ __forceinline__ void rotated(const uint4& u, const float (&sg)[8], int lane, float (&v)[8]) {
     unpack_bf16x8(u, v);
     if (ROT) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] *= sg[e];
-        fwht<D>(v, l);
+        fwht<D>(v, lane);
         const float f = inv_sqrt_d<D>();
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] *= f;
@@ -106,7 +145,7 @@ constexpr int kUnroll = 4;
 template <int D, bool ROT>
 __global__ __launch_bounds__(256) void amax_kernel(const uint16_t* x, const float* signs, int64_t rows, float* amax) {
     constexpr int LPR = D / 8, RPW = 64 / LPR, U = kUnroll;
-    const int lane = threadIdx.x & 63, l = lane % LPR;
+    const int lane = threadIdx.x & 63, l = row_pos<D>(lane);
     const int64_t waves = (int64_t)gridDim.x * (blockDim.x >> 6);
     const int64_t w = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     float sg[8];
@@ -115,7 +154,7 @@ __global__ __launch_bounds__(256) void amax_kernel(const uint16_t* x, const floa
     // (the loop runs on the wave's first row, the same for all its lanes: the
     // transform's lane exchanges need every lane; rows past the end are zeros)
     for (int64_t rb = w * RPW * U; rb < rows; rb += waves * RPW * U) {
-        const int64_t r0 = rb + lane / LPR;
+        const int64_t r0 = rb + row_of<D>(lane);
         uint4 u[U];
 #pragma unroll
         for (int k = 0; k < U; ++k) {
@@ -125,7 +164,7 @@ __global__ __launch_bounds__(256) void amax_kernel(const uint16_t* x, const floa
 #pragma unroll
         for (int k = 0; k < U; ++k) {
             float v[8];
-            rotated<D, ROT>(u[k], sg, l, v);
+            rotated<D, ROT>(u[k], sg, lane, v);
 #pragma unroll
             for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[e]));  // (fmaxf skips a NaN operand)
         }
@@ -163,7 +202,7 @@ template <int D, bool ROT>
 __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* x, const float* signs, int64_t rows,
                                                        const float* amax, uint8_t* x8, float* descale_out) {
     constexpr int LPR = D / 8, RPW = 64 / LPR, U = kUnroll;
-    const int lane = threadIdx.x & 63, l = lane % LPR;
+    const int lane = threadIdx.x & 63, l = row_pos<D>(lane);
     const float ds = descale_of(*amax);
     const float inv = 1.0f / ds;
     if (blockIdx.x == 0 && threadIdx.x == 0) *descale_out = ds;
@@ -174,7 +213,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* x, const 
     // (the loop runs on the wave's first row, the same for all its lanes: the
     // transform's lane exchanges need every lane; rows past the end are zeros)
     for (int64_t rb = w * RPW * U; rb < rows; rb += waves * RPW * U) {
-        const int64_t r0 = rb + lane / LPR;
+        const int64_t r0 = rb + row_of<D>(lane);
         uint4 u[U];
 #pragma unroll
         for (int k = 0; k < U; ++k) {
@@ -185,7 +224,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* x, const 
         for (int k = 0; k < U; ++k) {
             const int64_t r = r0 + k * RPW;
             float v[8];
-            rotated<D, ROT>(u[k], sg, l, v);
+            rotated<D, ROT>(u[k], sg, lane, v);
             const uint32_t lo = pack4_e4m3(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
             const uint32_t hi = pack4_e4m3(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
             if (r < rows) *reinterpret_cast<uint2*>(x8 + r * D + 8 * l) = make_uint2(lo, hi);
