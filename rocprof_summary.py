@@ -79,13 +79,13 @@ def dispatches(path, kernel_filter="attn_fwd_bf16_kernel"):
 
 def forward_kernel(w):
     """Name filter of the forward kernel that workload w launches."""
-    return "attn_fwd_f32_kernel" if WORKLOADS[w].dtype == "f32" else "attn_fwd_bf16_kernel"
+    return "attn_fwd_f32" if WORKLOADS[w].dtype == "f32" else "attn_fwd_bf16_kernel"
 
 
 # --------------------------------------------------------------------------- trace
 
 TRACE_LABELS = {
-    ("attn_fwd_f32_kernel<64, false>", 2): "forward, workload 1 (fp32): single-head B1 H1 N256 d64",
+    ("attn_fwd_f32_split_kernel<64, false, 8>", 8): "forward, workload 1 (fp32): single-head B1 H1 N256 d64",
     ("attn_fwd_bf16_kernel<64, 4, false, 2, false, false>", 256): "forward, workload 2: mha B4 H8 N1024 d64",
     ("attn_fwd_bf16_kernel<64, 4, true, 2, true, false>", 256): "forward, workload 3: causal B2 H8 N4096 d64",
     ("attn_fwd_bf16_kernel<128, 8, true, 1, false, false>", 1024): "forward, workload 4: causal long B1 H16 N16384 d128",
@@ -139,7 +139,8 @@ Command (one MI355X, repository root), summarised by `python3 rocprof_summary.py
     {cmd}
 
 Template arguments are attn_fwd_bf16_kernel <D, WAVES, CAUSAL, KSPLIT, PERSISTENT, GENERAL>
-(WAVES: 32-row query slices per key-split group) and attn_fwd_f32_kernel <D, CAUSAL>.
+(WAVES: 32-row query slices per key-split group) and attn_fwd_f32_split_kernel <D, CAUSAL,
+WAVES> (32 query rows, key tiles split over WAVES waves).
 Durations in microseconds from run_kernel_trace.csv (the warm-up launches are included in the
 plain average, not in the second).
 
@@ -268,7 +269,7 @@ short launches also count time outside the kernel).  Medians over the launches a
 The bf16 peak of 2.5 PFLOP/s assumes a 2.4 GHz clock: achieved TFLOP/s ≈ 2500 × (clock / 2.4)
 × MFMA busy × (algorithmic / executed MFMA flops) (workload 1: 157.3 in place of 2500).
 
-Workload 1 launches two workgroups: the shader engines without waves count no busy cycles, so
+Workload 1 launches eight workgroups: the shader engines without waves count no busy cycles, so
 its "clock" (cycles with waves present, averaged over all 32 engines) and "MFMA busy" are not
 utilisation figures of the chip; it is launch-latency bound.
 
