@@ -76,3 +76,39 @@ def test_noalloc_backward_rejects_problems_beyond_its_scratch(dev):
                                     q.data_ptr(), q.data_ptr(), q.data_ptr(), q.data_ptr(),
                                     1, 1, 1, N, 64, 0.125, 0, None, None)
     assert st == attn.ATTN_ERR_SCRATCH
+
+
+def test_noalloc_backward_replays_in_a_graph(dev):
+    """The callers this entry point is for include those that capture their
+    calls into a graph.  After one eager call (which looks up the scratch
+    array's address), the call is captured and replayed four times; between
+    replays the outputs are overwritten and another problem runs through the
+    same entry point (so the shared scratch holds other contents), and every
+    replay must give the eager gradients bit for bit."""
+    q, k, v, do, kl, scale, o, lse = _case(dev, 1, 4, 2, 500, 128, True, [437], 3)
+    q2, k2, v2, do2, kl2, scale2, o2, lse2 = _case(dev, 2, 2, 1, 200, 64, False, [200, 150], 4)
+    grads = tuple(torch.empty_like(t) for t in (q, k, v))
+    other = tuple(torch.empty_like(t) for t in (q2, k2, v2))
+
+    def call(stream):
+        st = attn.attn_bwd_bf16_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                                        lse.data_ptr(), grads[0].data_ptr(), grads[1].data_ptr(),
+                                        grads[2].data_ptr(), 1, 4, 2, 500, 128, scale, 1, kl.data_ptr(), stream)
+        assert st == attn.ATTN_OK, attn.attn_status_str(st)
+
+    call(torch.cuda.current_stream(dev).cuda_stream)
+    torch.cuda.synchronize()
+    eager = [g.clone() for g in grads]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(torch.cuda.current_stream(dev).cuda_stream)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for g in grads:
+            g.fill_(float("nan"))
+        attn.backward(q2, k2, v2, o2, lse2, do2, scale=scale2, key_lens=kl2, out=other, builtin_scratch=True)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, a, b in zip(("dq", "dk", "dv"), grads, eager):
+            assert torch.equal(a, b), f"replay {rep}: {name} differs from the eager call"
