@@ -21,7 +21,7 @@ Sources (web pages on exact tiled attention):
 * aifi page, PyTorch example: activations stored token-major with the heads
   side by side (``b n (h d)``), the layout of the packed-sequence oracle.
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
 causal admits keys j ≤ i; key padding admits j < key_len_b; grouped query
 heads map to kv head h // (H / Hkv); a row with no admissible key has O = 0
 and LSE = −∞; LSE is the natural-log log-sum-exp m + ln ℓ of the scaled
