@@ -305,6 +305,51 @@ __device__ __forceinline__ void qk_block(f32x16& s, const char* ks, const Offset
     }
 }
 
+// The same two products with the LDS operand reads split from the MFMAs, so
+// that the reads can be issued a step ahead of their use.
+template <int D, int W>
+using KOps = uint4[Geo<D, W>::DCH];  // the Sᵀ A operands of one 32-key block
+template <int D, int W>
+using VOps = bf16x8[Geo<D, W>::DBLK][2];  // the Oᵀ A operands of one 32-key block
+
+template <int D, int W>
+__device__ __forceinline__ void read_k(KOps<D, W>& a, const char* ks, const Offsets<D, W>& o, int blk) {
+#pragma unroll
+    for (int c = 0; c < Geo<D, W>::DCH; ++c)
+        a[c] = *reinterpret_cast<const uint4*>(ks + o.k_rd + blk * 32 * Cfg<D, W>::KROW + c * 32);
+}
+template <int D, int W>
+__device__ __forceinline__ void qk_mfma(f32x16& s, const KOps<D, W>& a, const bf16x8 (&qf)[Geo<D, W>::DCH]) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+    for (int c = 0; c < Geo<D, W>::DCH; ++c)
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[c]), qf[c], s, 0, 0, 0);
+}
+template <int D, int W>
+__device__ __forceinline__ void read_v(VOps<D, W>& va, const char* vs, const Offsets<D, W>& o, int blk) {
+    constexpr int VROW = Cfg<D, W>::VROW;
+#pragma unroll
+    for (int db = 0; db < Geo<D, W>::DBLK; ++db)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const char* at = vs + o.v_rd[db] + (32 * blk + 16 * c) * VROW;
+            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)at);
+            const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(at + 4 * VROW));
+            va[db][c] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+}
+template <int D, int W>
+__device__ __forceinline__ void pv_mfma(WaveState<D, W>& w, const VOps<D, W>& va, const uint32_t (&pb)[8]) {
+#pragma unroll
+    for (int db = 0; db < Geo<D, W>::DBLK; ++db)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const uint4 b = make_uint4(pb[4 * c], pb[4 * c + 1], pb[4 * c + 2], pb[4 * c + 3]);
+            w.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db][c], __builtin_bit_cast(bf16x8, b), w.acc[db], 0, 0, 0);
+        }
+}
+
 // One tile, one 32-key block at a time, software-pipelined so that each
 // step has matrix work independent of its vector work: step b issues the Sᵀ
 // MFMAs of block b + 1 and the Oᵀ MFMAs of block b − 1 (whose P is ready)
@@ -316,19 +361,38 @@ __device__ __forceinline__ void qk_block(f32x16& s, const char* ks, const Offset
 // tile, with that reference; MODE 2: exact running-max update on every
 // block (its α rescale of Oᵀ follows the previous block's Oᵀ MFMAs and
 // precedes this block's).
-template <int D, int W, bool CAUSAL, int MODE>
+template <int D, int W, bool CAUSAL, int MODE, bool AHEAD>
 __device__ __forceinline__ void tile(WaveState<D, W>& w, const char* stage, const Offsets<D, W>& o,
                                      const bf16x8 (&qf)[Geo<D, W>::DCH], float c2, bool masked, int kv0,
                                      int kv_len, int qrow, int hl, bool first) {
     constexpr int KBLK = Geo<D, W>::KBLK;
+    // AHEAD (d = 64 with two waves per SIMD, which leaves the registers):
+    // every operand of the tile is read at its start (the whole tile is in
+    // LDS after the barrier), so the reads' latency hides behind the first
+    // block's work
     f32x16 s[2];
     uint32_t pb[2][8];
-    qk_block<D, W>(s[0], stage, o, qf, 0);
+    KOps<D, W> ka[AHEAD ? KBLK : 1];
+    VOps<D, W> va[AHEAD ? KBLK : 1];
     const char* vs = stage + Cfg<D, W>::K_BYTES;
+    if constexpr (AHEAD) {
+#pragma unroll
+        for (int b = 0; b < KBLK; ++b) read_k<D, W>(ka[b], stage, o, b);
+#pragma unroll
+        for (int b = 0; b < KBLK; ++b) read_v<D, W>(va[b], vs, o, b);
+        qk_mfma<D, W>(s[0], ka[0], qf);
+    } else {
+        qk_block<D, W>(s[0], stage, o, qf, 0);
+    }
 #pragma unroll
     for (int blk = 0; blk < KBLK; ++blk) {
-        if (blk + 1 < KBLK) qk_block<D, W>(s[(blk + 1) & 1], stage, o, qf, blk + 1);
-        if (blk > 0) pv_block<D, W>(w, vs, o, blk - 1, pb[(blk - 1) & 1]);
+        if constexpr (AHEAD) {
+            if (blk + 1 < KBLK) qk_mfma<D, W>(s[(blk + 1) & 1], ka[blk + 1], qf);
+            if (blk > 0) pv_mfma<D, W>(w, va[blk - 1], pb[(blk - 1) & 1]);
+        } else {
+            if (blk + 1 < KBLK) qk_block<D, W>(s[(blk + 1) & 1], stage, o, qf, blk + 1);
+            if (blk > 0) pv_block<D, W>(w, vs, o, blk - 1, pb[(blk - 1) & 1]);
+        }
         f32x16& sb = s[blk & 1];
         if ((MODE == 2 || MODE == 3) && masked) apply_mask<CAUSAL, W>(sb, blk, kv0, kv_len, qrow, hl);
         if (MODE == 2) {
@@ -345,7 +409,8 @@ __device__ __forceinline__ void tile(WaveState<D, W>& w, const char* stage, cons
         }
         if (MODE == 1 || MODE == 4) __builtin_amdgcn_sched_barrier(0);  // keep the block pipeline order
     }
-    pv_block<D, W>(w, vs, o, KBLK - 1, pb[(KBLK - 1) & 1]);
+    if constexpr (AHEAD) pv_mfma<D, W>(w, va[KBLK - 1], pb[(KBLK - 1) & 1]);
+    else pv_block<D, W>(w, vs, o, KBLK - 1, pb[(KBLK - 1) & 1]);
 }
 
 // LDS stages: two separate __shared__ objects of KSPLIT stages each; group g
@@ -453,7 +518,7 @@ __device__ __forceinline__ void attend_tile(const Params& p, const Tile& t, cons
             const int kv0 = it * BC;
             if (it + KSPLIT < ntiles) load_tile<D, W>(o, next, kb, vb, kv0 + KSPLIT * BC, kv_len, ks, wave);
             if (MODE == 1 || MODE == 4) {
-                tile<D, W, CAUSAL, MODE>(w, cur, o, qf, c2, false, kv0, kv_len, qrow, hl, true);
+                tile<D, W, CAUSAL, MODE, D == 64 && KSPLIT == 2>(w, cur, o, qf, c2, false, kv0, kv_len, qrow, hl, true);
                 // eight waves: ℓ is complete here, otherwise the compiler sinks
                 // the first tile's row-sum adds of an unrolled pair into the
                 // second (its exponentials stay live across, and one tile of
@@ -463,7 +528,7 @@ __device__ __forceinline__ void attend_tile(const Params& p, const Tile& t, cons
             } else if (it < ntiles && !(CAUSAL && kv0 > q0w + 31 + dq)) {
                 // (under a causal mask a wave whose rows all precede the tile skips it)
                 const bool masked = (kv0 + BC > kv_len) || (CAUSAL && kv0 + BC - 1 > q0w + dq);
-                tile<D, W, CAUSAL, MODE>(w, cur, o, qf, c2, masked, kv0, kv_len, qrow + dq, hl, j == 0);
+                tile<D, W, CAUSAL, MODE, D == 64 && KSPLIT == 2>(w, cur, o, qf, c2, masked, kv0, kv_len, qrow + dq, hl, j == 0);
             }
             wait_loads();
             __syncthreads();
