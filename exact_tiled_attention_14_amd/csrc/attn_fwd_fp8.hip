@@ -232,6 +232,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_fp8_kernel(Params p) {
         load_tile8<D>(o, next2, spare, kb, vt, kv0 + 2 * BC, j + 2 < ntiles ? kv_len : 0, p.Nk, wave);
         if (!(CAUSAL && kv0 > q0w + 31)) {  // (a wave whose rows all precede the tile skips it)
             const bool masked = (kv0 + BC > kv_len) || (CAUSAL && kv0 + BC - 1 > q0w);
+            // the Vᵀ operands are read at the tile's start with the K operands,
+            // so that their latency hides behind the Sᵀ MFMAs and the softmax
+            i32x8 va[C::DBLK];
+#pragma unroll
+            for (int db = 0; db < C::DBLK; ++db) va[db] = read32(cur + C::K_BYTES + o.v_rd + db * 32 * C::VROW);
             f32x16 s[2];
 #pragma unroll
             for (int blk = 0; blk < 2; ++blk) {
@@ -296,10 +301,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_fp8_kernel(Params p) {
             i32x8 pb;
 #pragma unroll
             for (int i = 0; i < 8; ++i) pb[i] = (int)pk[i];
-            // all Vᵀ operands first, so that the P·V MFMAs issue back to back
-            i32x8 va[C::DBLK];
-#pragma unroll
-            for (int db = 0; db < C::DBLK; ++db) va[db] = read32(cur + C::K_BYTES + o.v_rd + db * 32 * C::VROW);
             if (masked) {
                 // keys at or past kv_len inside a 16-byte piece that was
                 // loaded: zero them (their P' is 0, but 0 · NaN is NaN)
