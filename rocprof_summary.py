@@ -6,6 +6,7 @@ the rocprofv3 commands it names in the summary it writes:
     python3 rocprof_summary.py trace   DIR LOG  # --kernel-trace --stats run of the default bench
     python3 rocprof_summary.py traffic BASE     # FETCH_SIZE / WRITE_SIZE passes (BASE/tr_*)
     python3 rocprof_summary.py util    BASE     # MFMA-busy passes (BASE/util_W)
+    python3 rocprof_summary.py valu    BASE     # vector-unit passes (BASE/valu_W)
 
 The raw runs (one MI355X, repository root, ``export TMPDIR=/tmp``; OUT is any
 output directory):
@@ -21,6 +22,10 @@ output directory):
         -d OUT/util_W -o run --output-format csv -- python3 bench.py --workload W \\
         --steps 20 --warmup 2 --no-extra --no-cpu-baseline --no-backward --no-varlen \\
         --no-splitkv --no-fp8                              (W = 1..5)
+    rocprofv3 --kernel-trace --pmc SQ_ACTIVE_INST_VALU SQ_INSTS_VALU SQ_INSTS_VALU_TRANS_F32 \\
+        SQ_INSTS_MFMA SQ_INSTS_LDS SQ_ACTIVE_INST_LDS SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES \\
+        -d OUT/valu_W -o run --output-format csv -- python3 bench.py --workload W --steps 20 \\
+        --warmup 2 --no-extra --no-cpu-baseline --no-backward --no-varlen --no-splitkv --no-fp8  (W = 2..5)
 
 This is measurement tooling: it reads CSV files and imports bench.py for the
 workload definitions, algorithmic byte counts and the kernel source hash.
@@ -283,6 +288,63 @@ Kernel source hash (bench.kernel_source_hash): `{out['kernel_source_hash']}`.
     print(md)
 
 
+# --------------------------------------------------------------------------- vector unit
+
+VALU_COUNTERS = ("SQ_ACTIVE_INST_VALU SQ_INSTS_VALU SQ_INSTS_VALU_TRANS_F32 SQ_INSTS_MFMA SQ_INSTS_LDS "
+                 "SQ_ACTIVE_INST_LDS SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES")
+
+
+def valu(base):
+    lines = []
+    out = {"kernel_source_hash": bench.kernel_source_hash(), "workloads": {}}
+    for w in (2, 3, 4, 5):
+        per, dur = dispatches(csv_in(os.path.join(base, f"valu_{w}"), "run_counter_collection.csv"), forward_kernel(w))
+        recs = []
+        for d, c in sorted(per.items()):
+            cycles = c["SQ_BUSY_CYCLES"] / SES                      # shader cycles with waves present
+            mfma_n = c["SQ_INSTS_MFMA"]
+            recs.append({
+                "valu_per_mfma": c["SQ_INSTS_VALU"] / mfma_n if mfma_n else float("nan"),
+                "trans_per_mfma": c["SQ_INSTS_VALU_TRANS_F32"] / mfma_n if mfma_n else float("nan"),
+                "lds_per_mfma": c["SQ_INSTS_LDS"] / mfma_n if mfma_n else float("nan"),
+                # SQ_ACTIVE_INST_* count quad-cycles per wave, summed over the waves of each SIMD
+                "valu_busy": 4 * c["SQ_ACTIVE_INST_VALU"] / SIMDS / cycles,
+                "lds_busy": 4 * c["SQ_ACTIVE_INST_LDS"] / SIMDS / cycles,
+                "mfma_busy": c["SQ_VALU_MFMA_BUSY_CYCLES"] / SIMDS / cycles,
+            })
+        recs = recs[1:] if len(recs) > 2 else recs
+        med = {k: statistics.median(r[k] for r in recs) for k in recs[0]}
+        out["workloads"][str(w)] = {k: round(v, 4) for k, v in med.items()}
+        lines.append(f"| {w} | {WORKLOADS[w].name} | {med['valu_per_mfma']:.2f} | {med['trans_per_mfma']:.2f} | "
+                     f"{med['lds_per_mfma']:.2f} | {100 * med['valu_busy']:.1f}% | {100 * med['mfma_busy']:.1f}% | "
+                     f"{100 * med['lds_busy']:.1f}% |")
+    md = f"""# Vector-unit activity of attn_fwd_bf16_kernel beside its MFMA activity (rocprofv3 counters)
+
+Command per workload W (one MI355X, repository root), summarised by
+`python3 rocprof_summary.py valu {base}`:
+
+    rocprofv3 --kernel-trace --pmc {VALU_COUNTERS} -d {base}/valu_W -o run --output-format csv -- python3 bench.py --workload W --steps 20 --warmup 2 {BENCH_FLAGS}
+
+Per launch (medians over the launches after the first): instructions per MFMA instruction from
+`SQ_INSTS_VALU` (every vector instruction, MFMAs included), `SQ_INSTS_VALU_TRANS_F32` (the
+exponentials) and `SQ_INSTS_LDS`; busy fractions of one SIMD from `SQ_ACTIVE_INST_VALU` and
+`SQ_ACTIVE_INST_LDS` (quad-cycles a wave spends on such instructions, summed over the SIMD's waves,
+so a fraction above the unit's share means waves overlap) and `SQ_VALU_MFMA_BUSY_CYCLES`, each over
+`SQ_BUSY_CYCLES` / 32 (shader cycles with waves present) and 1024 SIMDs.  `SQ_INSTS_VALU` counts the
+MFMAs too, so "VALU instr per MFMA" is one more than the vector instructions issued per MFMA; a
+32x32x16 bf16 MFMA holds the matrix core 32 cycles, about what six or seven plain vector
+instructions take to issue.
+
+Kernel source hash (bench.kernel_source_hash): `{out['kernel_source_hash']}`.
+
+| workload | name | VALU instr per MFMA | exp per MFMA | LDS instr per MFMA | VALU-active | MFMA busy | LDS-active |
+|---|---|---|---|---|---|---|---|
+""" + "\n".join(lines) + "\n"
+    with open(os.path.join(PROFILES, "attn_fwd_workloads2-5_valu.md"), "w") as f:
+        f.write(md)
+    print(md)
+
+
 if __name__ == "__main__":
     mode = sys.argv[1] if len(sys.argv) > 1 else ""
     if mode == "trace" and len(sys.argv) == 4:
@@ -291,5 +353,7 @@ if __name__ == "__main__":
         traffic(sys.argv[2])
     elif mode == "util" and len(sys.argv) == 3:
         util(sys.argv[2])
+    elif mode == "valu" and len(sys.argv) == 3:
+        valu(sys.argv[2])
     else:
         sys.exit(__doc__)
